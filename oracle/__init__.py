@@ -1,0 +1,17 @@
+"""FP64 CPU reference ("oracle") of the BF16 hyper-connection read.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
+package. The product path (``bf16_hyper_connection_amd``) never imports it,
+and the two share no code: no kernels, headers, helpers, tables or constants.
+"""
+
+from .reference import (  # noqa: F401
+    EPS,
+    bf16_bits_to_f64,
+    down_projection,
+    epilogue,
+    hc_read,
+    stream_rms_scale,
+    up_projection,
+)
