@@ -1,0 +1,175 @@
+"""Benchmark of the BF16 hyper-connection read on one MI355X.
+
+Workload (the cold-weight T sweep): real geometry (4 streams x 2560, R = 320,
+13,107,200 bytes of BF16 weights per read), 32 independent weight sets
+(419 MB, more than the 256 MB MALL) rotated call by call, T = 1..8 tokens,
+x ~ N(0, 1), no pending write or injection.  One step = for T = 1..8, one read
+per weight set (256 reads), captured once as a HIP graph and replayed; inputs
+are resident in HBM before the timed region starts.
+
+Prints ONE JSON line: value = microseconds per read over the whole step
+(lower is better), per-T microseconds and algorithmic GB/s, the roofline of
+the read, and the FP64 CPU reference timed on the host as a baseline.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per cold HC read (norm+down+up) at T=1..8; achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+S, D, R, TMAX = 4, 2560, 320, 8
+W_BYTES = 2 * R * S * D * 2
+
+
+def algorithmic_bytes(T, pending=False, inj=False):
+    """Weights once + w_norm + x read + out and mean written (+ pending, + inj)."""
+    b = W_BYTES + S * D * 4 + T * (S * D * 4 + S * D * 4 + D * 4)
+    if pending:
+        b += T * S * D * 4
+    if inj:
+        b += T * R * 4
+    return b
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The FP64 reference, as it stands, on a bounded sample of the same sweep (host cores)."""
+    import oracle
+    from bf16_hyper_connection_amd import inputs as gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    ws = [gen.weight_set(2, k) for k in range(4)]
+    xs = {T: gen.cold_sweep_x(T) for T in range(1, TMAX + 1)}
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for T in range(1, TMAX + 1):
+            w = ws[n % len(ws)]
+            oracle.hc_read(xs[T], w.w_norm, w.w_down, w.w_up)
+            n += 1
+    el = time.perf_counter() - t0
+    return {"value": round(el / n * 1e6, 1), "unit": "µs per read", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} reads of the same sweep (T = 1..8 in turn, 4 of the 32 weight sets), "
+                      f"{el:.1f} s of float64 numpy on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this read runs on one GPU only (asked for --gpus {args.gpus}); "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bf16_hyper_connection_amd import hcr
+    from bf16_hyper_connection_amd import inputs as gen
+    if not os.path.exists(hcr.LIB_PATH):
+        from bf16_hyper_connection_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+
+    log(f"bench: generating {args.sets} weight sets")
+    readers = []
+    for k in range(args.sets):
+        w = gen.weight_set(2, k)
+        readers.append(hcr.HCRead(torch.from_numpy(w.w_down.view(np.int16)).to(dev),
+                                  torch.from_numpy(w.w_up.view(np.int16)).to(dev),
+                                  torch.from_numpy(w.w_norm).to(dev)))
+    xs = {T: torch.from_numpy(gen.cold_sweep_x(T)).to(dev) for T in range(1, TMAX + 1)}
+    outs = {T: torch.empty((T, S, D), device=dev) for T in xs}
+    means = {T: torch.empty((T, D), device=dev) for T in xs}
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def capture(Ts, calls_per_T):
+        g = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for T in Ts:
+                    for i in range(calls_per_T):
+                        readers[i % len(readers)].read(xs[T], out=outs[T], mean=means[T])
+        torch.cuda.current_stream().wait_stream(stream)
+        return g
+
+    def timed(g, reps, warm):
+        with torch.cuda.stream(stream):
+            for _ in range(warm):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1)  # ms
+
+    # per-T: 32 rotated reads per graph, replayed 10 times (320 calls per T)
+    per_T_us, per_T_gbps = {}, {}
+    for T in range(1, TMAX + 1):
+        g = capture([T], len(readers))
+        ms = timed(g, 10, 2)
+        us = ms * 1000.0 / (10 * len(readers))
+        per_T_us[T] = round(us, 3)
+        per_T_gbps[T] = round(algorithmic_bytes(T) / us / 1e3, 1)
+        log(f"bench: T={T} {us:.3f} us/read  {per_T_gbps[T]:.0f} GB/s")
+        del g
+
+    # the timed steps: the whole sweep per step
+    g = capture(range(1, TMAX + 1), len(readers))
+    reads_per_step = TMAX * len(readers)
+    timed(g, args.warmup, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(g, args.steps, 0)
+    wall = time.perf_counter() - t0
+    ms_per_step = ms / args.steps
+    us_per_read = ms_per_step * 1000.0 / reads_per_step
+    bytes_step = sum(algorithmic_bytes(T) for T in range(1, TMAX + 1)) * len(readers)
+    achieved = bytes_step / (ms_per_step * 1e-3) / 1e9
+    log(f"bench: {args.steps} steps in {wall:.3f} s wall, {ms_per_step:.3f} ms/step, {us_per_read:.3f} us/read")
+
+    line = {
+        "metric": METRIC, "value": round(us_per_read, 3), "unit": "µs", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "cold HC read T sweep: 4 streams x 2560, R = 320, 32 rotated BF16 weight sets "
+                               "(419 MB), T = 1..8, one read per set and T per step, HIP graph replay",
+                   "reads_per_step": reads_per_step, "weight_sets": len(readers),
+                   "accumulate": "fp32 (bf16 MFMA operands, activations split into bf16 high + low)",
+                   "per_T_us": per_T_us, "per_T_algorithmic_GBps": per_T_gbps},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "one read = hc_down + hc_up dispatches; event-timed per read over the timed region"},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the FP64 reference on the host")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

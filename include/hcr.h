@@ -1,0 +1,106 @@
+/*
+ * hcr.h -- C ABI of the BF16 hyper-connection read (HC read) for MI355X (gfx950).
+ *
+ * The operation (Strata PR #2812, "sycl: STRATA_GR_FUSED=1, the two-kernel
+ * BF16 hyper-connection read (opt-in)", sections Summary and What changed;
+ * Strata PR #2070, Turing kernels for the hyper-connection read, first
+ * comment): for each of T tokens of a speculative-decode verify window, the
+ * S = 4 residual streams of d = 2560 values are RMS-normalised per stream,
+ * projected down to R = 320 values (lo, plus an optional injection),
+ * projected back up to S x d values, and finished by the epilogue (an
+ * optional pending write, a sigmoid gate per stream, the stream mean).
+ * Per token t, stream s, column c, down row r, up row j = s*d + c:
+ *
+ *   rs[t,s]    = 1 / sqrt(mean_c x[t,s,c]^2 + 1e-6)
+ *   lo[t,r]    = sum_s rs[t,s] * sum_c W_down[r, s*d+c] * x[t,s,c] * w_norm[s,c]  (+ inj[t,r])
+ *   u[t,j]     = sum_k W_up[j,k] * lo[t,k]
+ *   out[t,s,c] = pending[t,s,c] (or 0) + sigmoid(lo[t,s]) * u[t, s*d+c]
+ *   mean[t,c]  = (1/4) * sum_s out[t,s,c]
+ *
+ * Arithmetic is FP32 (BF16 weights are widened exactly); summation orders
+ * are fixed, so a call is bitwise reproducible, also as a replayed HIP graph.
+ *
+ * Memory. Every pointer is a device pointer the caller owns (the library
+ * allocates nothing on the device and never frees caller memory).  Layouts
+ * are contiguous, token-major, fixed strides:
+ *   x, pending, out : float [T][4][2560]
+ *   mean            : float [T][2560]
+ *   inj             : float [T][320]
+ *   w_down          : BF16  [320][10240]  row-major, column block s = stream s
+ *   w_up            : BF16  [10240][320]  row-major, row s*2560 + c
+ *   w_norm          : float [4][2560]
+ *   scratch         : hcr_scratch_bytes() bytes, 256-byte aligned, one per handle
+ * Every pointer but scratch must be 16-byte aligned.
+ *
+ * Errors. Functions return HCR_OK (0) or a negative code; hcr_strerror()
+ * names it.  All argument checks run on the host before any HIP call, so a
+ * rejected call has no effect on the device.  There is no fallback path.
+ */
+#ifndef HCR_H
+#define HCR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HCR_STREAMS 4      /* residual streams S */
+#define HCR_STREAM_D 2560  /* values per stream d */
+#define HCR_RANK 320       /* down-projection rows R (up-projection K) */
+#define HCR_T_MAX 8        /* tokens per read */
+
+enum {
+  HCR_OK = 0,
+  HCR_EINVAL = -1,   /* null handle/pointer, or T outside 0..HCR_T_MAX */
+  HCR_EALIGN = -2,   /* a pointer is not 16-byte (scratch: 256-byte) aligned */
+  HCR_ESCRATCH = -3, /* scratch smaller than hcr_scratch_bytes() */
+  HCR_EALIAS = -4,   /* buffers overlap in a way the read does not allow */
+  HCR_EHIP = -5      /* a HIP launch failed (hipGetLastError after the launches) */
+};
+
+typedef struct hcr_handle* hcr_t;
+
+/* Bytes of device scratch one handle needs (partial sums, sums of squares, lo, rs). */
+size_t hcr_scratch_bytes(void);
+
+/* Byte offsets, inside a handle's scratch, of the last read's lo (float [T][320])
+ * and rs (float [T][4]); valid after the read's kernels complete. */
+int hcr_scratch_layout(size_t* lo_offset, size_t* rs_offset);
+
+/* Geometry compiled into the library (any argument may be NULL). */
+int hcr_geometry(int* streams, int* stream_d, int* rank, int* t_max);
+
+/* Create a handle for one weight set (one layer half: w_down, w_up, w_norm) and
+ * its scratch.  Host-only: records pointers, makes no HIP call.  The weights and
+ * the scratch must stay valid until hcr_destroy.  Errors: HCR_EINVAL (a NULL
+ * pointer), HCR_EALIGN, HCR_ESCRATCH, HCR_EALIAS (scratch overlaps a weight). */
+int hcr_create(const void* w_down, const void* w_up, const float* w_norm,
+               void* scratch, size_t scratch_bytes, hcr_t* out);
+
+/* One HC read of T tokens, asynchronous on `stream` (a hipStream_t; NULL is the
+ * null stream).  Enqueues two kernels and returns; no host synchronisation,
+ * allocation or memset, so it can be captured into a HIP graph.
+ *   x        [T][4][2560]  read only
+ *   pending  [T][4][2560]  or NULL (no pending write)
+ *   inj      [T][320]      or NULL (no injection)
+ *   out      [T][4][2560]  written; may be exactly x or exactly pending,
+ *                          otherwise must not overlap any other buffer
+ *   mean     [T][2560]     written; must not overlap any other buffer
+ * T = 0 is an empty read: nothing is enqueued.  Reads on one handle share its
+ * scratch and must be ordered on one stream; distinct handles are independent.
+ * Errors: HCR_EINVAL, HCR_EALIGN, HCR_EALIAS (all before any HIP call), HCR_EHIP. */
+int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj,
+             float* out, float* mean, void* stream);
+
+/* Free the host-side handle (never the caller's device memory).  NULL is a no-op. */
+void hcr_destroy(hcr_t h);
+
+/* Static text naming an error code. */
+const char* hcr_strerror(int rc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCR_H */

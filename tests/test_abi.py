@@ -1,0 +1,115 @@
+"""The C ABI on the host: the library loads, exports what include/hcr.h declares, and
+rejects bad arguments before any HIP call (no GPU is used by these tests)."""
+
+import ctypes
+
+import pytest
+
+from bf16_hyper_connection_amd import hcr
+from tests.libhcr_util import declared_functions, ensure_built
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"hcr_create", "hcr_read", "hcr_destroy", "hcr_scratch_bytes", "hcr_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libhcr.so does not export {n}"
+
+
+def test_geometry_and_scratch(lib):
+    assert hcr.hcr_geometry() == (4, 2560, 320, 8)
+    n = hcr.hcr_scratch_bytes()
+    lo, rs = hcr.hcr_scratch_layout()
+    assert n % 256 == 0 and lo % 256 == 0 and rs % 256 == 0
+    assert lo + 8 * 320 * 4 <= rs and rs + 8 * 4 * 4 <= n
+
+
+def test_strerror(lib):
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert hcr.hcr_strerror(rc) and hcr.hcr_strerror(rc) != hcr.hcr_strerror(-99)
+
+
+# Fake, never-dereferenced device addresses: the checks below fail before any HIP call.
+MB = 1 << 20
+WD, WU, WN, SC = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+X, P, I, O, M = 0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+
+def _create(**kw):
+    a = dict(w_down=WD, w_up=WU, w_norm=WN, scratch=SC, scratch_bytes=hcr.hcr_scratch_bytes())
+    a.update(kw)
+    return hcr.hcr_create(a["w_down"], a["w_up"], a["w_norm"], a["scratch"], a["scratch_bytes"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(w_down=None), hcr.HCR_EINVAL),
+    (dict(w_up=None), hcr.HCR_EINVAL),
+    (dict(w_norm=None), hcr.HCR_EINVAL),
+    (dict(scratch=None), hcr.HCR_EINVAL),
+    (dict(w_down=WD + 8), hcr.HCR_EALIGN),
+    (dict(w_norm=WN + 4), hcr.HCR_EALIGN),
+    (dict(scratch=SC + 16), hcr.HCR_EALIGN),
+    (dict(scratch_bytes=1024), hcr.HCR_ESCRATCH),
+    (dict(scratch=WD + MB), hcr.HCR_EALIAS),       # inside w_down
+])
+def test_create_rejects(lib, kw, rc):
+    with pytest.raises(hcr.HCRError) as e:
+        _create(**kw)
+    assert e.value.rc == rc
+
+
+def test_create_null_out(lib):
+    assert lib.hcr_create(ctypes.c_void_p(WD), ctypes.c_void_p(WU), ctypes.c_void_p(WN), ctypes.c_void_p(SC),
+                          hcr.hcr_scratch_bytes(), None) == hcr.HCR_EINVAL
+
+
+T_BYTES = 4 * 2560 * 4
+
+
+@pytest.mark.parametrize("T,args,rc", [
+    (9, {}, hcr.HCR_EINVAL),
+    (-1, {}, hcr.HCR_EINVAL),
+    (2, dict(x=None), hcr.HCR_EINVAL),
+    (2, dict(out=None), hcr.HCR_EINVAL),
+    (2, dict(mean=None), hcr.HCR_EINVAL),
+    (2, dict(x=X + 4), hcr.HCR_EALIGN),
+    (2, dict(pending=P + 8), hcr.HCR_EALIGN),
+    (2, dict(inj=I + 12), hcr.HCR_EALIGN),
+    (2, dict(mean=M + 4), hcr.HCR_EALIGN),
+    (2, dict(out=X + 16), hcr.HCR_EALIAS),             # partial overlap with x
+    (2, dict(out=P + T_BYTES), hcr.HCR_EALIAS),        # partial overlap with pending (T = 2)
+    (2, dict(mean=O + 64), hcr.HCR_EALIAS),            # mean inside out
+    (2, dict(mean=X), hcr.HCR_EALIAS),                 # mean on x
+    (2, dict(out=SC), hcr.HCR_EALIAS),                 # out on the scratch
+    (2, dict(out=WU), hcr.HCR_EALIAS),                 # out on the weights
+    (2, dict(inj=SC + 256), hcr.HCR_EALIAS),           # inj on the scratch
+    (2, dict(mean=I), hcr.HCR_EALIAS),                 # mean on inj
+])
+def test_read_rejects_before_any_hip_call(lib, T, args, rc):
+    h = _create()
+    try:
+        a = dict(x=X, pending=P, inj=I, out=O, mean=M)
+        a.update(args)
+        got = hcr.hcr_read(h, T, a["x"], a["pending"], a["inj"], a["out"], a["mean"], None)
+        assert got == rc, (got, hcr.hcr_strerror(got))
+    finally:
+        hcr.hcr_destroy(h)
+
+
+def test_read_null_handle_and_empty(lib):
+    assert hcr.hcr_read(None, 1, X, None, None, O, M, None) == hcr.HCR_EINVAL
+    h = _create()
+    try:
+        # T = 0: an empty read enqueues nothing, even with null buffers
+        assert hcr.hcr_read(h, 0, None, None, None, None, None, None) == hcr.HCR_OK
+    finally:
+        hcr.hcr_destroy(h)
+
+
+def test_destroy_null_is_noop(lib):
+    hcr.hcr_destroy(None)

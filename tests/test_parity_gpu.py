@@ -1,0 +1,213 @@
+"""Parity of the HIP read (through the C ABI) with the FP64 reference, on the GPU.
+
+Every case runs at the real geometry (4 streams x 2560, R = 320) and compares
+every element of out, mean and lo with the reference, within 1e-4 of the
+largest |value| of each tensor (rs within 1e-5 relative).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bf16_hyper_connection_amd import inputs as gen
+from tests import oracle_pins as pins
+from tests.gpu_util import check_read, dev, reader_for, to_dev
+from tests.libhcr_util import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+@pytest.fixture(scope="module")
+def wset():
+    w = gen.weight_set(1, 0)
+    return w, reader_for(w)
+
+
+def _read(reader, x, p, inj):
+    out, mean = reader.read(to_dev(x), to_dev(p), to_dev(inj))
+    return out, mean
+
+
+@pytest.mark.parametrize("T", range(1, 9))
+@pytest.mark.parametrize("with_pending", [False, True])
+@pytest.mark.parametrize("with_inj", [False, True])
+def test_matrix(wset, T, with_pending, with_inj):
+    """T = 1..8 x pending write on/off x injection on/off (32 cases), one weight set."""
+    w, reader = wset
+    x = gen.activations(1, T, index=T)
+    p = gen.pending(1, T, index=T) if with_pending else None
+    inj = gen.injection(1, T, index=T) if with_inj else None
+    out, mean = _read(reader, x, p, inj)
+    ref = oracle.hc_read(x, w.w_norm, w.w_down, w.w_up, pending=p, inj=inj)
+    check_read(reader, T, out, mean, ref, f"T={T} pending={with_pending} inj={with_inj}")
+
+
+def test_single_read_seed0():
+    """Real geometry, T = 1, one weight set, no pending write or injection (seed 0)."""
+    c = gen.single_read(0)
+    w = c["weights"][0]
+    r = reader_for(w)
+    out, mean = _read(r, c["x"], None, None)
+    check_read(r, 1, out, mean, oracle.hc_read(c["x"], w.w_norm, w.w_down, w.w_up), "single read")
+
+
+def test_full_epilogue_32_sets():
+    """T = 4, pending write and injection on, 32 weight sets (seed 7)."""
+    c = gen.full_epilogue(7)
+    for k, w in enumerate(c["weights"]):
+        r = reader_for(w)
+        out, mean = _read(r, c["x"][k], c["pending"][k], c["inj"][k])
+        ref = oracle.hc_read(c["x"][k], w.w_norm, w.w_down, w.w_up, pending=c["pending"][k], inj=c["inj"][k])
+        check_read(r, 4, out, mean, ref, f"full epilogue set {k}")
+
+
+def test_numerics_stress_32_sets():
+    """T = 8, heavy-tailed x (stream RMS 1e-3..1e3), near-duplicate W_down rows, pending and inj on."""
+    c = gen.numerics_stress(5)
+    worst = 0.0
+    for k, w in enumerate(c["weights"]):
+        r = reader_for(w)
+        out, mean = _read(r, c["x"][k], c["pending"][k], c["inj"][k])
+        ref = oracle.hc_read(c["x"][k], w.w_norm, w.w_down, w.w_up, pending=c["pending"][k], inj=c["inj"][k])
+        errs = check_read(r, 8, out, mean, ref, f"stress set {k}")
+        worst = max(worst, max(errs.values()))
+    print(f"numerics stress: worst error {worst:.3e} of max |ref|")
+
+
+def test_cold_rotation_all_sets_all_T():
+    """The timed workload's launch pattern: 32 weight sets rotated per call, T = 1..8, each call checked."""
+    ws = gen.cold_sweep_weights(32)
+    readers = [reader_for(w) for w in ws]
+    for T in range(1, 9):
+        x = gen.cold_sweep_x(T)
+        xd = to_dev(x)
+        for k, (w, r) in enumerate(zip(ws, readers)):
+            out, mean = r.read(xd)
+            ref = oracle.hc_read(x, w.w_norm, w.w_down, w.w_up)
+            check_read(r, T, out, mean, ref, f"rotation T={T} set {k}")
+
+
+def test_closed_form_identity_weights():
+    """Identity-like weights at the real geometry: the HIP read against the reference and the closed form."""
+    (x, wn, wd, wu, p, inj), closed = pins.closed_form_case(4, 2560, 320, 3)
+    w = gen.WeightSet(wd, wu, wn)
+    r = reader_for(w)
+    out, mean = _read(r, x, p, inj)
+    ref = oracle.hc_read(x, wn, wd, wu, pending=p, inj=inj)
+    check_read(r, 3, out, mean, ref, "closed form vs reference")
+    check_read(r, 3, out, mean, closed, "closed form vs formula")
+
+
+def test_zero_stream_and_saturated_gates(wset):
+    w, reader = wset
+    T = 5
+    x = gen.activations(3, T)
+    x[:, 1, :] = 0.0  # a zero stream: rs = 1000, no contribution
+    inj = gen.injection(3, T)
+    inj[:, 0] = 100.0   # gate of stream 0 open (sigmoid = 1)
+    inj[:, 2] = -100.0  # gate of stream 2 shut (sigmoid ~ 0)
+    p = gen.pending(3, T)
+    out, mean = _read(reader, x, p, inj)
+    ref = oracle.hc_read(x, w.w_norm, w.w_down, w.w_up, pending=p, inj=inj)
+    check_read(reader, T, out, mean, ref, "zero stream / saturated gates")
+    torch.cuda.synchronize()
+    # the shut gate leaves the pending write (up to sigmoid(-100) * |u|)
+    assert np.max(np.abs(out[:, 2].cpu().numpy() - p[:, 2])) <= 1e-30
+
+
+def test_all_zero_input(wset):
+    """x = 0 everywhere: rs = 1000, lo = inj = 0, out = pending + 0.5 * 0."""
+    w, reader = wset
+    T = 2
+    x = np.zeros((T, 4, 2560), np.float32)
+    p = gen.pending(4, T)
+    out, mean = _read(reader, x, p, None)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.from_numpy(p))
+    lo, rs = reader.last_lo_rs(T)
+    assert torch.all(lo == 0) and torch.allclose(rs.cpu(), torch.full((T, 4), 1000.0))
+
+
+def test_empty_read_leaves_outputs(wset):
+    _, reader = wset
+    x = torch.empty((0, 4, 2560), device=dev())
+    out = torch.full((0, 4, 2560), 7.0, device=dev())
+    mean = torch.full((0, 2560), 7.0, device=dev())
+    reader.read(x, out=out, mean=mean)
+    torch.cuda.synchronize()
+
+
+def test_in_place_out_on_x_and_on_pending(wset):
+    w, reader = wset
+    T = 6
+    x = gen.activations(5, T)
+    p = gen.pending(5, T)
+    inj = gen.injection(5, T)
+    ref_out, ref_mean = _read(reader, x, p, inj)
+    xd = to_dev(x)
+    out1, mean1 = reader.read(xd, to_dev(p), to_dev(inj), out=xd)
+    pd = to_dev(p)
+    out2, mean2 = reader.read(to_dev(x), pd, to_dev(inj), out=pd)
+    torch.cuda.synchronize()
+    assert out1.data_ptr() == xd.data_ptr() and out2.data_ptr() == pd.data_ptr()
+    for o, m in ((out1, mean1), (out2, mean2)):
+        assert torch.equal(o, ref_out) and torch.equal(m, ref_mean)
+
+
+def test_repeated_reads_bitwise(wset):
+    w, reader = wset
+    T = 7
+    xd, pd, idd = to_dev(gen.activations(6, T)), to_dev(gen.pending(6, T)), to_dev(gen.injection(6, T))
+    o0, m0 = reader.read(xd, pd, idd)
+    o0, m0 = o0.clone(), m0.clone()
+    for _ in range(100):
+        o, m = reader.read(xd, pd, idd)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(m, m0)
+
+
+def test_token_results_do_not_depend_on_T(wset):
+    """Each token's result is the same, bit for bit, whether it is read alone or in a window of 8."""
+    w, reader = wset
+    T = 8
+    x, p, inj = gen.activations(8, T), gen.pending(8, T), gen.injection(8, T)
+    o8, m8 = _read(reader, x, p, inj)
+    o8, m8 = o8.clone(), m8.clone()
+    for t in range(T):
+        o1, m1 = _read(reader, x[t:t + 1], p[t:t + 1], inj[t:t + 1])
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o8[t]) and torch.equal(m1[0], m8[t]), f"token {t}"
+
+
+@pytest.mark.parametrize("T", [1, 6, 8])
+def test_graph_replay_bitwise(wset, T):
+    """A captured read replayed several times (with eager work between) equals the direct call, bitwise."""
+    w, reader = wset
+    xd, pd, idd = to_dev(gen.activations(9, T)), to_dev(gen.pending(9, T)), to_dev(gen.injection(9, T))
+    direct_o, direct_m = reader.read(xd, pd, idd)
+    direct_o, direct_m = direct_o.clone(), direct_m.clone()
+    out = torch.empty_like(direct_o)
+    mean = torch.empty_like(direct_m)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            reader.read(xd, pd, idd, out=out, mean=mean)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.fill_(float("nan"))
+        mean.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, direct_o) and torch.equal(mean, direct_m), f"replay {i}"
+        # eager work between replays, on other buffers
+        reader.read(to_dev(gen.activations(10 + i, T)))
+        torch.cuda.synchronize()
