@@ -13,6 +13,7 @@ the read, and the FP64 CPU reference timed on the host as a baseline.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +38,31 @@ def algorithmic_bytes(T, pending=False, inj=False):
     if inj:
         b += T * R * 4
     return b
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hc_read_cold_sweep_traffic.json")
+KERNEL_SOURCES = ["hcr_kernels.hip", "hcr_layout.h", "hcr_api.cpp"]
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources of the read; counter-derived figures are valid only for this hash."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bf16_hyper_connection_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per read from the committed counter summary, or None if the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_read_mean_T1_8")
 
 
 def log(*a):
@@ -73,6 +99,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this read runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -150,6 +178,14 @@ def main():
     bytes_step = sum(algorithmic_bytes(T) for T in range(1, TMAX + 1)) * len(readers)
     achieved = bytes_step / (ms_per_step * 1e-3) / 1e9
     log(f"bench: {args.steps} steps in {wall:.3f} s wall, {ms_per_step:.3f} ms/step, {us_per_read:.3f} us/read")
+    if args.calibrate_copy:
+        src = torch.ones(16 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: calibration copy of 64 MiB done (4 launches)")
+    traffic = measured_traffic()
 
     line = {
         "metric": METRIC, "value": round(us_per_read, 3), "unit": "µs", "n_gpus": 1,
@@ -159,11 +195,13 @@ def main():
         "config": {"workload": "cold HC read T sweep: 4 streams x 2560, R = 320, 32 rotated BF16 weight sets "
                                "(419 MB), T = 1..8, one read per set and T per step, HIP graph replay",
                    "reads_per_step": reads_per_step, "weight_sets": len(readers),
-                   "accumulate": "fp32 (bf16 MFMA operands, activations split into bf16 high + low)",
+                   "arithmetic": "bf16 weights; fp32 accumulation (down: FMA on widened weights; "
+                                 "up: v_dot2_f32_bf16 with lo split into bf16 high + low)",
                    "per_T_us": per_T_us, "per_T_algorithmic_GBps": per_T_gbps},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "one read = hc_down + hc_up dispatches; event-timed per read over the timed region"},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "the read (hc_down + hc_up dispatches), event-timed per read over the timed region; "
+                               "traffic = counter-measured HBM bytes per read (mean over T = 1..8)"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the FP64 reference on the host")

@@ -4,36 +4,47 @@
 // changed; Strata PR #2070, Turing hyper-connection read kernels) is split in
 // two launches that each stream one 6.55 MB BF16 matrix once for all T tokens:
 //
-//   hc_down<T>: norm statistics + down projection.  A work-group owns 16 rows
-//     of W_down and one 1,280-column slab (half a stream).  It stages the T
-//     tokens' weighted stream values x*w_norm unscaled in LDS, already split
-//     into BF16 high and low parts in MFMA operand order, and the slab's sums
-//     of squares; each wave multiplies its 16 x 320 weight tile with
-//     v_mfma_f32_16x16x32_bf16, where the 16 MFMA columns are the 8 tokens'
-//     high parts and their 8 low parts.  The four waves' tiles are added in a
-//     fixed order and the slab partial sums (unscaled) are written to scratch.
-//   hc_up<T>: split-reduction finish + up projection + epilogue.  Every
-//     work-group first issues its W_up loads, then finishes the down reduction
-//     itself from the 8 slab partials (rs per stream from the slab sums of
-//     squares, the injection added), which are small and L2-resident, then
-//     multiplies 16 W_up rows per wave (4 columns of each of the 4 streams)
-//     with lo, split the same way, and applies the epilogue: pending write,
-//     sigmoid gate of lo[t][s], stream mean.
+//   hc_down<T>: norm statistics + down projection + split-reduction finish.
+//     A work-group owns one whole stream (2,560 columns) of 5 W_down rows, so
+//     it can apply rs itself: every lane owns 10 columns (one 16-byte chunk
+//     and one dword of each row, both coalesced across the wave), computes
+//     x*w_norm and the sums of squares of its columns for the T tokens, and
+//     one FP32 FMA chain per (row, token) over the exactly widened BF16
+//     weights.  The 6T per-lane values are summed over the wave (halving with
+//     v_permlane32/16_swap, then DPP) and over the 4 waves (LDS, fixed order);
+//     the work-group writes rs[t][s] * (row sums), one partial per stream.
+//   hc_up<T, INJ, PEND>: lo[t][k] = the 4 stream partials (+ injection), then
+//     40 rows of W_up (10 columns x 4 streams) per work-group.  Each row is
+//     reduced by the 32 lanes of a half-wave; lane q owns K [8q, 8q+8) and
+//     [256+2q, +2) and multiplies with v_dot2_f32_bf16 against lo split into
+//     BF16 high and low parts.  Epilogue: pending write, sigmoid gate of
+//     lo[t][s], stream mean of 4 adjacent outputs (DPP quad).
 //
-// Why BF16 high/low operands: the activations are FP32.  Rounding them to
-// BF16 once loses ~2^-9 relative, far above the read's 1e-4 tolerance; the
-// high part plus the BF16-rounded remainder keep ~2^-17, and BF16 x BF16
-// products are exact in the FP32 accumulator.
+// Why v_dot2 on high/low parts of lo: the activations are FP32.  Rounding lo
+// to BF16 once loses ~2^-9 relative, above the read's 1e-4 tolerance; the
+// high part plus the BF16-rounded remainder keep ~2^-17.  The down
+// projection uses FMA on widened weights instead: its activations change
+// every row group, and the split would cost more VALU than the widening.
+//
+// Why not MFMA: the T <= 8 tokens fill at most half of a 16-wide MFMA tile,
+// and on MI355X the two-kernel read was measured ~1.5 us slower with
+// v_mfma_f32_16x16x32_bf16 tiles than with this VALU path at T = 1..5 (and
+// within 0.3 us at T = 6..8), the arithmetic being a small part of a
+// latency-bound read.
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
 // counter plus the finisher's reads cost several microseconds per launch
-// (cross-XCD release/acquire), more than reading the 8 partials again in the
-// next launch, whose weight loads are in flight meanwhile.
+// (cross-XCD release/acquire).  Here the down work-group covers a whole
+// stream, and the up kernel adds the 4 stream partials itself while its
+// weight loads are in flight.
 //
-// Determinism: every sum has a fixed order (MFMA accumulation over fixed
-// chunks, waves added 0+1+2+3, slabs added per stream in order), so repeated
-// calls and graph replays are bitwise identical.
+// Loads: vector-memory loads complete in issue order, so every kernel issues
+// its small inputs first (x, w_norm; partials, injection, pending) and its
+// weight tile after them, all before any arithmetic.
+//
+// Determinism: every sum has a fixed order, so repeated calls and graph
+// replays are bitwise identical, and each token's result does not depend on T.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,13 +53,7 @@
 
 namespace hcr {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-
-__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                 c, 0, 0, 0);
-}
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -71,249 +76,318 @@ __device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint
 }
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-__device__ __forceinline__ f32x4 shfl_xor4(f32x4 v, int m) {
-  f32x4 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] = __shfl_xor(v[q], m, 64);
-  return r;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+__device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// ---------------------------------------------------------------------------
-// down: partial sums of one (16-row block, 1,280-column slab) tile
-// ---------------------------------------------------------------------------
+// Sum N values per lane over the 64 lanes of a wave (N a multiple of 4).  Two
+// halving steps (v_permlane32_swap, v_permlane16_swap) then a butterfly inside
+// each row of 16 lanes; afterwards every lane l holds, in v[0 .. N/4), the
+// totals of values (l >> 4) * N/4 + i.  The order of the additions is fixed.
+template <int N>
+__device__ __forceinline__ void wave_sum(float (&v)[N]) {
+  static_assert(N % 4 == 0, "wave_sum needs a multiple of 4 values");
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // lanes < 32: value i; lanes >= 32: value i + N/2
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 4]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // even rows: value i; odd rows: value i + N/4
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    v[i] += dpp<0xB1>(v[i]);   // quad_perm [1,0,3,2]
+    v[i] += dpp<0x4E>(v[i]);   // quad_perm [2,3,0,1]
+    v[i] += dpp<0x141>(v[i]);  // row_half_mirror
+    v[i] += dpp<0x140>(v[i]);  // row_mirror
+  }
+}
+
+constexpr int round4(int n) { return (n + 3) & ~3; }
+
+// down: one stream x 5 rows per work-group; rs applied here (the work-group sees the whole stream)
 template <int T>
-__global__ __launch_bounds__(THREADS) void hc_down(const uint4* __restrict__ w_down, const float* __restrict__ x,
-                                                   const float* __restrict__ w_norm, float* __restrict__ part,
-                                                   float* __restrict__ ssq) {
-  // Work-group b takes slab b % 8: consecutive work-groups go to consecutive
-  // XCDs, so all row blocks of one slab share an XCD's L2 for x and w_norm.
-  const int slab = blockIdx.x % NSLAB;
-  const int rb = blockIdx.x / NSLAB;
+__global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restrict__ w_down,
+                                                           const float* __restrict__ x,
+                                                           const float* __restrict__ w_norm,
+                                                           float* __restrict__ part, float* __restrict__ rs_out) {
+  // consecutive work-groups take consecutive streams: the XCD of work-group b (b mod 8) sees one stream
+  const int s = blockIdx.x & (S - 1);
+  const int g = blockIdx.x >> 2;  // rows DOWN_ROWS*g ..
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, lg = lane >> 4;
-  const int stream = slab / SLABS_PER_STREAM;
-  const int scol0 = (slab % SLABS_PER_STREAM) * SLAB;  // first column of the slab inside its stream
+  const int ca = 512 * wave + 8 * lane;         // 8 columns: one 16-byte chunk per row
+  const int cb = 2048 + 128 * wave + 2 * lane;  // 2 columns: one dword per row
 
-  // Vector-memory loads complete in issue order, so the small loads the staging
-  // needs (x, w_norm) are issued first and the weight tile after them: the
-  // staging then waits only for its own data while the weights stream in.
-  constexpr int ITEMS = T * (SLAB / 8);  // (token, 8-column chunk) staging items
-  constexpr int NI = (ITEMS + THREADS - 1) / THREADS;
-  f32x4 xv[NI][2], nv[NI][2];
+  // 1. x and w_norm first (vector loads complete in issue order), then the 5 weight rows
+  f32x4 xa0[T], xa1[T];
+  f32x2 xb[T];
 #pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int q = tid + n * THREADS;
-    if (q < ITEMS) {
-      const int t = q / (SLAB / 8), c8 = q % (SLAB / 8);
-      const float* xp = x + ((size_t)t * S + stream) * D + scol0 + 8 * c8;
-      const float* np = w_norm + stream * D + scol0 + 8 * c8;
-      xv[n][0] = ld4(xp);
-      xv[n][1] = ld4(xp + 4);
-      nv[n][0] = ld4(np);
-      nv[n][1] = ld4(np + 4);
+  for (int t = 0; t < T; ++t) {
+    const float* xt = x + ((size_t)t * S + s) * D;
+    xa0[t] = ld4(xt + ca);
+    xa1[t] = ld4(xt + ca + 4);
+    xb[t] = ld2(xt + cb);
+  }
+  const float* ns = w_norm + s * D;
+  const f32x4 na0 = ld4(ns + ca), na1 = ld4(ns + ca + 4);
+  const f32x2 nb = ld2(ns + cb);
+  const uint16_t* wr = w_down + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
+  uint4 wa[DOWN_ROWS];
+  uint32_t wb[DOWN_ROWS];
+#pragma unroll
+  for (int r = 0; r < DOWN_ROWS; ++r) {
+    wa[r] = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
+    wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. activations x*w_norm (unscaled) and the lane's sums of squares
+  constexpr int N = round4((DOWN_ROWS + 1) * T);
+  float act[T][10];
+  float v[N];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      act[t][e] = xa0[t][e] * na0[e];
+      act[t][4 + e] = xa1[t][e] * na1[e];
+    }
+    act[t][8] = xb[t][0] * nb[0];
+    act[t][9] = xb[t][1] * nb[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa0[t][e], xa0[t][e], ss);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa1[t][e], xa1[t][e], ss);
+    ss = __builtin_fmaf(xb[t][0], xb[t][0], ss);
+    ss = __builtin_fmaf(xb[t][1], xb[t][1], ss);
+    v[DOWN_ROWS * T + t] = ss;
+  }
+#pragma unroll
+  for (int i = (DOWN_ROWS + 1) * T; i < N; ++i) v[i] = 0.f;
+
+  // 3. per row: the BF16 weights widened exactly to FP32, one FMA chain per token
+#pragma unroll
+  for (int r = 0; r < DOWN_ROWS; ++r) {
+    const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
+    float wv[10];
+#pragma unroll
+    for (int e = 0; e < 5; ++e) {
+      wv[2 * e] = __uint_as_float(u[e] << 16);
+      wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 10; ++e) a = __builtin_fmaf(wv[e], act[t][e], a);
+      v[r * T + t] = a;
     }
   }
 
-  // 1. the tile's weights: lane (li, lg) holds row 16*rb + li, 80 contiguous columns
-  const uint4* wp = w_down + ((size_t)(rb * ROWS_WG + li) * DD + slab * SLAB + wave * DOWN_WAVE_COLS +
-                              lg * DOWN_LANE_COLS) / 8;
-  uint4 a[DOWN_CHUNKS];
+  // 4. sums over the wave, then over the 4 waves in a fixed order
+  wave_sum<N>(v);
+  __shared__ float wsum[DOWN_THREADS / 64][N];
+  __shared__ float tot[N];
+  if ((lane & 15) == 0) {
 #pragma unroll
-  for (int m = 0; m < DOWN_CHUNKS; ++m) a[m] = wp[m];
-
-  // 2. stage x*w_norm (unscaled) as BF16 high/low MFMA operands, and sums of squares
-  //    bop[w][m][g][j]: the 16 bytes lane (j, g) of wave w feeds MFMA m
-  __shared__ uint4 bop[DOWN_WAVES][DOWN_CHUNKS][4][16];
-  __shared__ float ss_part[TMAX][SLAB / 8];
-  __shared__ f32x4 ctile[DOWN_WAVES][64];
-  // operands of absent tokens (T..7) are zero
-  for (int q = tid; q < (TMAX - T) * (SLAB / 8); q += THREADS) {
-    const int t = T + q / (SLAB / 8), c8 = q % (SLAB / 8);
-    const int w = c8 / (DOWN_CHUNKS * 4), g = (c8 / DOWN_CHUNKS) % 4, m = c8 % DOWN_CHUNKS;
-    bop[w][m][g][t] = make_uint4(0, 0, 0, 0);
-    bop[w][m][g][t + 8] = make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int q = tid + n * THREADS;
-    if (q < ITEMS) {
-      const int t = q / (SLAB / 8), c8 = q % (SLAB / 8);
-      const int w = c8 / (DOWN_CHUNKS * 4), g = (c8 / DOWN_CHUNKS) % 4, m = c8 % DOWN_CHUNKS;
-      float v[8];
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = xv[n][0][e] * nv[n][0][e];
-        v[4 + e] = xv[n][1][e] * nv[n][1][e];
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xv[n][h][e], xv[n][h][e], ss);
-      uint4 hi, lo;
-      split_hi_lo(v, hi, lo);
-      bop[w][m][g][t] = hi;
-      bop[w][m][g][t + 8] = lo;
-      ss_part[t][c8] = ss;
-    }
+    for (int i = 0; i < N / 4; ++i) wsum[wave][(lane >> 4) * (N / 4) + i] = v[i];
   }
   __syncthreads();
-
-  // 3. 16 rows x 320 columns per wave on the matrix cores
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < DOWN_CHUNKS; ++m) acc = mfma16x16x32(a[m], bop[wave][m][lg][li], acc);
-  // lane (li, lg) holds rows 4*lg .. 4*lg+3 of the block for MFMA column li
-  ctile[wave][lane] = acc;
+  if (tid < N) tot[tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
   __syncthreads();
 
-  if (wave == 0) {
-    // 4. waves added in a fixed order, then high + low parts of each token
-    f32x4 c = ((ctile[0][lane] + ctile[1][lane]) + ctile[2][lane]) + ctile[3][lane];
-    const f32x4 other = shfl_xor4(c, 8);
-    if (li < T) st4(part + ((size_t)slab * TMAX + li) * R + rb * ROWS_WG + 4 * lg, c + other);
-  } else if (wave == 1 && rb == 0) {
-    // 5. the slab's sum of squares per token (one row block writes it):
-    //    lane = 8*t + p sums columns chunks [20p, 20p+20), then p is reduced by a fixed tree
-    const int t = lane >> 3, p = lane & 7;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < (SLAB / 8) / 8; ++i) s += ss_part[t][p * ((SLAB / 8) / 8) + i];
-    s += __shfl_xor(s, 4, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 1, 64);
-    if (p == 0 && t < T) ssq[slab * TMAX + t] = s;
+  // 5. rs of this stream per token, and the rs-scaled partial sums of the 5 rows
+  if (tid < DOWN_ROWS * T) {
+    const int r = tid / T, t = tid % T;
+    const float rs = 1.0f / __builtin_sqrtf(tot[DOWN_ROWS * T + t] * (1.0f / D) + 1e-6f);
+    part[((size_t)s * TMAX + t) * R + DOWN_ROWS * g + r] = rs * tot[r * T + t];
+    if (g == 0 && r == 0) rs_out[t * S + s] = rs;
   }
 }
 
-// ---------------------------------------------------------------------------
-// up: finish the down reduction, up projection, epilogue
-// ---------------------------------------------------------------------------
-template <int T, bool INJ, bool PEND>
-__global__ __launch_bounds__(THREADS) void hc_up(const uint4* __restrict__ w_up, const float* __restrict__ part,
-                                                 const float* __restrict__ ssq, const float* __restrict__ inj,
-                                                 const float* pending, float* out, float* __restrict__ mean,
-                                                 float* __restrict__ lo_out, float* __restrict__ rs_out) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, lg = lane >> 4;
-  const int c0 = blockIdx.x * UP_WG_COLS + wave * UP_WAVE_COLS;  // this wave's 4 columns
-
-  // Vector-memory loads complete in issue order: the small inputs of the
-  // prologue and the epilogue (sums of squares, slab partials, injection,
-  // pending write) are issued before the weights so that the prologue waits
-  // only for them while W_up streams in.
-  constexpr int ITEMS = T * (R / 4);  // (token, 4 K values) items of lo
-  constexpr int NI = (ITEMS + THREADS - 1) / THREADS;
-  float ssv[SLABS_PER_STREAM] = {};
-  if (tid < T * S) {
-    const int t = tid / S, s = tid % S;
+// Sum N values per lane over the 32 lanes of each half-wave (N even): one halving
+// step (v_permlane16_swap) then a butterfly inside each row of 16 lanes.  Lanes
+// of row (l >> 4) & 1 then hold, in v[0 .. N/2), the half-wave totals of values
+// ((l >> 4) & 1) * N/2 + i.
+template <int N>
+__device__ __forceinline__ void half_wave_sum(float (&v)[N]) {
+  static_assert(N % 2 == 0, "half_wave_sum needs an even number of values");
 #pragma unroll
-    for (int k = 0; k < SLABS_PER_STREAM; ++k) ssv[k] = ssq[(s * SLABS_PER_STREAM + k) * TMAX + t];
+  for (int i = 0; i < N / 2; ++i) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
   }
-  f32x4 pv[NI][NSLAB], iv[NI];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    v[i] += dpp<0xB1>(v[i]);
+    v[i] += dpp<0x4E>(v[i]);
+    v[i] += dpp<0x141>(v[i]);
+    v[i] += dpp<0x140>(v[i]);
+  }
+}
+
+constexpr int round2(int n) { return (n + 1) & ~1; }
+
+// up: lo = sum of the 4 stream partials (+ injection); 40 rows of W_up (10 columns x 4 streams) per work-group
+template <int T, bool INJ, bool PEND>
+__global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_up,
+                                                         const float* __restrict__ part,
+                                                         const float* __restrict__ inj, const float* pending,
+                                                         float* out, float* __restrict__ mean,
+                                                         float* __restrict__ lo_out) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, q = lane & 31;  // half-wave (row of the iteration), K lane
+  const int c0 = blockIdx.x * UP_COLS;
+
+  // 1. small loads first (vector loads complete in issue order): stream partials and injection
+  //    for lo, pending for the epilogue
+  constexpr int ITEMS = T * (R / 4);  // (token, 4 K values)
+  constexpr int NI = (ITEMS + UP_THREADS - 1) / UP_THREADS;
+  f32x4 pv[NI][S], iv[NI];
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
-    const int q = tid + n * THREADS;
-    if (q < ITEMS) {
-      const int t = q / (R / 4), k = 4 * (q % (R / 4));
+    const int it = tid + n * UP_THREADS;
+    if (it < ITEMS) {
+      const int t = it / (R / 4), k = 4 * (it % (R / 4));
 #pragma unroll
-      for (int sl = 0; sl < NSLAB; ++sl) pv[n][sl] = ld4(part + ((size_t)sl * TMAX + t) * R + k);
+      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
       if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
     }
   }
-  const int te = li;  // the epilogue token of this lane
-  f32x4 pend = {0.f, 0.f, 0.f, 0.f};
-  if (PEND && te < T) pend = ld4(pending + ((size_t)te * S + lg) * D + c0);
-
-  // 1. the wave's 16 W_up rows: row li = stream li/4, column c0 + li%4; lane group lg holds K [80lg, 80lg+80)
-  const uint4* wp = w_up + ((size_t)((li >> 2) * D + c0 + (li & 3)) * R + lg * UP_LANE_K) / 8;
-  uint4 a[UP_CHUNKS];
+  // epilogue: output o = (t * UP_COLS + cc) * 4 + s, the 4 streams of a column in an aligned quad of lanes
+  constexpr int NO = (T * UP_ROWS + UP_THREADS - 1) / UP_THREADS;
+  float pend[NO];
 #pragma unroll
-  for (int m = 0; m < UP_CHUNKS; ++m) a[m] = wp[m];
-
-  __shared__ float rs_sm[TMAX][S];
-  __shared__ float lo_sm[TMAX][R];
-  __shared__ uint4 bop[UP_CHUNKS][4][16];
-
-  // 2. rs per (token, stream) from the slab sums of squares
-  if (tid < T * S) {
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < SLABS_PER_STREAM; ++k) ss += ssv[k];
-    rs_sm[tid / S][tid % S] = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + 1e-6f);
+  for (int n = 0; n < NO; ++n) {
+    const int o = tid + n * UP_THREADS;
+    pend[n] = 0.f;
+    if (PEND && o < T * UP_ROWS) {
+      const int t = o / UP_ROWS, cc = (o / S) % UP_COLS, s = o % S;
+      pend[n] = pending[((size_t)t * S + s) * D + c0 + cc];
+    }
   }
-  __syncthreads();
 
-  // 3. lo[t][k] = sum_s rs[t][s] * (slab partials of stream s, in order) + inj[t][k]
+  // 2. weights: iteration m, half h -> row rw = 10*wave + 2m + h (column rw >> 2, stream rw & 3);
+  //    lane q owns K [8q, 8q+8) (one 16-byte chunk) and [256 + 2q, 256 + 2q + 2) (one dword)
+  uint4 wa[UP_ITERS];
+  uint32_t wb[UP_ITERS];
+  const uint16_t* wu16 = reinterpret_cast<const uint16_t*>(w_up);
+#pragma unroll
+  for (int m = 0; m < UP_ITERS; ++m) {
+    const int rw = UP_WAVE_ROWS * wave + 2 * m + h;
+    const uint16_t* row = wu16 + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
+    wa[m] = *reinterpret_cast<const uint4*>(row + 8 * q);
+    wb[m] = *reinterpret_cast<const uint32_t*>(row + 256 + 2 * q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  __shared__ __attribute__((aligned(16))) float lo_sm[TMAX * R];
+  __shared__ uint4 acta_sm[2][TMAX][32];  // K [8q, 8q+8): high, low parts
+  __shared__ uint2 actb_sm[TMAX][32];     // K [256+2q, +2): (high, low)
+  __shared__ float gate_sm[TMAX][S];
+  __shared__ float u_sm[TMAX][UP_ROWS];
+
+  // 3. lo[t][k] = ((p0 + p1) + p2) + p3 (+ inj)
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
-    const int q = tid + n * THREADS;
-    if (q < ITEMS) {
-      const int t = q / (R / 4), k = 4 * (q % (R / 4));
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    const int it = tid + n * UP_THREADS;
+    if (it < ITEMS) {
+      const int t = it / (R / 4), k = 4 * (it % (R / 4));
+      f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
+      if (INJ) vv += iv[n];
+      *reinterpret_cast<f32x4*>(lo_sm + t * R + k) = vv;
+    }
+  }
+  __syncthreads();
+  // 4. lo as BF16 high/low v_dot2 operands, in each lane's K order; gates; lo for inspection
+  if (tid < T * 32) {
+    const int t = tid >> 5, qq = tid & 31;
+    float va[8];
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        f32x4 ps = pv[n][s * SLABS_PER_STREAM];
+    for (int e = 0; e < 8; ++e) va[e] = lo_sm[t * R + 8 * qq + e];
+    uint4 hi, lo;
+    split_hi_lo(va, hi, lo);
+    acta_sm[0][t][qq] = hi;
+    acta_sm[1][t][qq] = lo;
+    const f32x2 vb = {lo_sm[t * R + 256 + 2 * qq], lo_sm[t * R + 256 + 2 * qq + 1]};
+    const bf16x2 bh = __builtin_convertvector(vb, bf16x2);
+    const bf16x2 bl = __builtin_convertvector(vb - __builtin_convertvector(bh, f32x2), bf16x2);
+    actb_sm[t][qq] = make_uint2(__builtin_bit_cast(uint32_t, bh), __builtin_bit_cast(uint32_t, bl));
+  }
+  if (tid < T * S) gate_sm[tid / S][tid % S] = 1.0f / (1.0f + expf(-lo_sm[(tid / S) * R + (tid % S)]));
+  if (blockIdx.x == 0)
+    for (int i = tid; i < T * R; i += UP_THREADS) lo_out[i] = lo_sm[i];
+  __syncthreads();
+
+  // 5. dot products: per (iteration, token) the lane's 10 K values, high then low part of lo
+  constexpr int N = round2(UP_ITERS * T);
+  float v[N];
 #pragma unroll
-        for (int kk = 1; kk < SLABS_PER_STREAM; ++kk) ps += pv[n][s * SLABS_PER_STREAM + kk];
-        v += rs_sm[t][s] * ps;
+  for (int i = UP_ITERS * T; i < N; ++i) v[i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint4 ah = acta_sm[0][t][q], al = acta_sm[1][t][q];
+    const uint2 ab = actb_sm[t][q];
+    const uint32_t hh[5] = {ah.x, ah.y, ah.z, ah.w, ab.x};
+    const uint32_t ll[5] = {al.x, al.y, al.z, al.w, ab.y};
+#pragma unroll
+    for (int m = 0; m < UP_ITERS; ++m) {
+      const uint32_t w[5] = {wa[m].x, wa[m].y, wa[m].z, wa[m].w, wb[m]};
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < 5; ++d) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w[d]), __builtin_bit_cast(bf16x2v, hh[d]), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w[d]), __builtin_bit_cast(bf16x2v, ll[d]), acc, false);
       }
-      if (INJ) v += iv[n];
-      *reinterpret_cast<f32x4*>(&lo_sm[t][k]) = v;
+      v[m * T + t] = acc;
+    }
+  }
+
+  // 6. each row over its half-wave; row (lane >> 4) & 1 of the half holds values [((lane >> 4) & 1) * N/2, +N/2)
+  half_wave_sum<N>(v);
+  if ((lane & 15) == 0) {
+    const int base = ((lane >> 4) & 1) * (N / 2);
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const int j = base + i;  // value j = m * T + t of row 10*wave + 2m + h
+      if (j < UP_ITERS * T) u_sm[j % T][UP_WAVE_ROWS * wave + 2 * (j / T) + h] = v[i];
     }
   }
   __syncthreads();
 
-  // 4. lo as BF16 high/low MFMA operands: bop[m][g][j] = part j of K [80g + 8m, +8)
-  for (int q = tid; q < UP_CHUNKS * 4 * 16; q += THREADS) {
-    const int j = q & 15, g = (q >> 4) & 3, m = q >> 6;
-    const int t = j & 7;
-    uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
-    if (t < T) {
-      float v[8];
+  // 7. epilogue: out = pending + sigmoid(lo[t][s]) * u; stream mean over the quad (fixed order)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = lo_sm[t][g * UP_LANE_K + 8 * m + e];
-      split_hi_lo(v, hi, lo);
+  for (int n = 0; n < NO; ++n) {
+    const int o = tid + n * UP_THREADS;
+    const bool has = o < T * UP_ROWS;
+    const int t = has ? o / UP_ROWS : 0, cc = (o / S) % UP_COLS, s = o % S;
+    float val = 0.f;
+    if (has) {
+      val = gate_sm[t][s] * u_sm[t][S * cc + s];
+      if (PEND) val += pend[n];
+      out[((size_t)t * S + s) * D + c0 + cc] = val;
     }
-    const bool high = j < 8;
-    bop[m][g][j] = make_uint4(high ? hi.x : lo.x, high ? hi.y : lo.y, high ? hi.z : lo.z, high ? hi.w : lo.w);
-  }
-  __syncthreads();
-
-  // 5. 16 rows x 320 K on the matrix cores
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < UP_CHUNKS; ++m) acc = mfma16x16x32(a[m], bop[m][lg][li], acc);
-  // lane (li, lg): column li (token li%8, high or low part), rows 4lg..4lg+3 = stream lg, columns c0..c0+3
-  const f32x4 u = acc + shfl_xor4(acc, 8);
-
-  // 6. epilogue: out = pending + sigmoid(lo[t][s]) * u; mean over the 4 streams in a fixed order
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  if (te < T) {
-    const float gate = 1.0f / (1.0f + expf(-lo_sm[te][lg]));
-    o = gate * u;
-    if (PEND) o += pend;
-    st4(out + ((size_t)te * S + lg) * D + c0, o);
-  }
-  const f32x4 m1 = o + shfl_xor4(o, 16);    // streams (0+1) and (2+3)
-  const f32x4 m2 = m1 + shfl_xor4(m1, 32);  // (0+1) + (2+3)
-  if (te < T && lg == 0) st4(mean + (size_t)te * D + c0, 0.25f * m2);
-
-  // 7. the read's lo and rs, kept in the scratch for inspection (one work-group)
-  if (blockIdx.x == 0) {
-    for (int q = tid; q < T * R; q += THREADS) lo_out[q] = lo_sm[q / R][q % R];
-    if (tid < T * S) rs_out[tid] = rs_sm[tid / S][tid % S];
+    const float m1 = val + dpp<0xB1>(val);  // streams (0+1), (2+3)
+    const float m2 = m1 + dpp<0x4E>(m1);    // (0+1) + (2+3)
+    if (has && s == 0) mean[(size_t)t * D + c0 + cc] = 0.25f * m2;
   }
 }
 
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-typedef void (*down_fn)(const uint4*, const float*, const float*, float*, float*);
-typedef void (*up_fn)(const uint4*, const float*, const float*, const float*, const float*, float*, float*,
-                      float*, float*);
+typedef void (*down_fn)(const uint16_t*, const float*, const float*, float*, float*);
+typedef void (*up_fn)(const uint4*, const float*, const float*, const float*, float*, float*, float*);
 
 static const down_fn kDown[TMAX] = {hc_down<1>, hc_down<2>, hc_down<3>, hc_down<4>,
                                     hc_down<5>, hc_down<6>, hc_down<7>, hc_down<8>};
@@ -328,14 +402,13 @@ int launch_read(int T, const void* w_down, const void* w_up, const float* w_norm
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* sc = static_cast<char*>(scratch);
   float* part = reinterpret_cast<float*>(sc + OFF_PART);
-  float* ssq = reinterpret_cast<float*>(sc + OFF_SSQ);
   float* lo = reinterpret_cast<float*>(sc + OFF_LO);
   float* rs = reinterpret_cast<float*>(sc + OFF_RS);
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
-  hipLaunchKernelGGL(kDown[T - 1], dim3(DOWN_WGS), dim3(THREADS), 0, st, static_cast<const uint4*>(w_down), x,
-                     w_norm, part, ssq);
-  hipLaunchKernelGGL(kUp[T - 1][inj != nullptr][pending != nullptr], dim3(UP_WGS), dim3(THREADS), 0, st, static_cast<const uint4*>(w_up), part, ssq,
-                     inj, pending, out, mean, lo, rs);
+  hipLaunchKernelGGL(kDown[T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, static_cast<const uint16_t*>(w_down),
+                     x, w_norm, part, rs);
+  hipLaunchKernelGGL(kUp[T - 1][inj != nullptr][pending != nullptr], dim3(UP_WGS), dim3(UP_THREADS), 0, st,
+                     static_cast<const uint4*>(w_up), part, inj, pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }
 
