@@ -99,6 +99,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-window", action="store_true", help="skip the 96-read verify window measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -187,6 +188,40 @@ def main():
         log("bench: calibration copy of 64 MiB done (4 launches)")
     traffic = measured_traffic()
 
+    window = None
+    if not args.no_window:
+        # the verify window: 96 chained reads (out_i = x_{i+1}), distinct weight sets, T = 6, pending on
+        del g
+        n_win, t_win = 96, 6
+        log(f"bench: generating the {n_win}-read verify window")
+        cw = gen.verify_window(n_win, t_win)
+        wreaders = [hcr.HCRead(torch.from_numpy(w.w_down.view(np.int16)).to(dev),
+                               torch.from_numpy(w.w_up.view(np.int16)).to(dev),
+                               torch.from_numpy(w.w_norm).to(dev)) for w in cw["weights"]]
+        del cw["weights"]
+        wpend = [torch.from_numpy(p_).to(dev) for p_ in cw["pending"]]
+        wx0 = torch.from_numpy(cw["x0"]).to(dev)
+        wouts = [torch.empty((t_win, S, D), device=dev) for _ in range(n_win)]
+        wmeans = [torch.empty((t_win, D), device=dev) for _ in range(n_win)]
+        gw = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gw, stream=stream):
+                xx = wx0
+                for i, r in enumerate(wreaders):
+                    r.read(xx, wpend[i], None, out=wouts[i], mean=wmeans[i])
+                    xx = wouts[i]
+        torch.cuda.current_stream().wait_stream(stream)
+        reps = 50
+        wms = timed(gw, reps, 3) / reps
+        wbytes = n_win * algorithmic_bytes(t_win, pending=True)
+        window = {"reads": n_win, "T": t_win, "pending": True, "us_per_window": round(wms * 1000, 2),
+                  "us_per_read": round(wms * 1000 / n_win, 3),
+                  "algorithmic_GBps": round(wbytes / (wms * 1e-3) / 1e9, 1),
+                  "note": "one HIP graph of the 96-read residual chain, distinct BF16 weight sets (1.26 GB)"}
+        log(f"bench: window {window['us_per_window']} us ({window['us_per_read']} us/read, "
+            f"{window['algorithmic_GBps']} GB/s)")
+
     line = {
         "metric": METRIC, "value": round(us_per_read, 3), "unit": "µs", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -197,7 +232,8 @@ def main():
                    "reads_per_step": reads_per_step, "weight_sets": len(readers),
                    "arithmetic": "bf16 weights; fp32 accumulation (down: FMA on widened weights; "
                                  "up: v_dot2_f32_bf16 with lo split into bf16 high + low)",
-                   "per_T_us": per_T_us, "per_T_algorithmic_GBps": per_T_gbps},
+                   "per_T_us": per_T_us, "per_T_algorithmic_GBps": per_T_gbps,
+                   "verify_window": window},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "the read (hc_down + hc_up dispatches), event-timed per read over the timed region; "

@@ -186,6 +186,36 @@ def test_token_results_do_not_depend_on_T(wset):
         assert torch.equal(o1[0], o8[t]) and torch.equal(m1[0], m8[t]), f"token {t}"
 
 
+def test_numerics_stress_graph_replay_bitwise():
+    """The stress workload's reads captured in one graph: replays equal the direct calls bit for bit."""
+    c = gen.numerics_stress(5, n_sets=8)
+    readers = [reader_for(w) for w in c["weights"]]
+    xs = [to_dev(x) for x in c["x"]]
+    ps = [to_dev(p) for p in c["pending"]]
+    ij = [to_dev(i) for i in c["inj"]]
+    outs = [torch.empty((8, 4, 2560), device=dev()) for _ in readers]
+    means = [torch.empty((8, 2560), device=dev()) for _ in readers]
+    for k, r in enumerate(readers):
+        r.read(xs[k], ps[k], ij[k], out=outs[k], mean=means[k])
+    torch.cuda.synchronize()
+    direct = [(o.clone(), m.clone()) for o, m in zip(outs, means)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for k, r in enumerate(readers):
+                r.read(xs[k], ps[k], ij[k], out=outs[k], mean=means[k])
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, m) in enumerate(direct):
+            assert torch.equal(outs[k], o) and torch.equal(means[k], m), f"replay {rep} read {k}"
+
+
 @pytest.mark.parametrize("T", [1, 6, 8])
 def test_graph_replay_bitwise(wset, T):
     """A captured read replayed several times (with eager work between) equals the direct call, bitwise."""
