@@ -110,7 +110,7 @@ void hcr_destroy(hcr_t h) { free(h); }
 const char* hcr_strerror(int rc) {
   switch (rc) {
     case HCR_OK: return "ok";
-    case HCR_EINVAL: return "invalid argument (null handle or pointer, or T outside 0..8)";
+    case HCR_EINVAL: return "invalid argument (null handle or pointer, or T outside 0..HCR_T_MAX)";
     case HCR_EALIGN: return "misaligned pointer (16 bytes; scratch 256 bytes)";
     case HCR_ESCRATCH: return "scratch smaller than hcr_scratch_bytes()";
     case HCR_EALIAS: return "buffers overlap in a way the read does not allow";

@@ -26,11 +26,15 @@
 // projection uses FMA on widened weights instead: its activations change
 // every row group, and the split would cost more VALU than the widening.
 //
-// Why not MFMA: the T <= 8 tokens fill at most half of a 16-wide MFMA tile,
-// and on MI355X the two-kernel read was measured ~1.5 us slower with
-// v_mfma_f32_16x16x32_bf16 tiles than with this VALU path at T = 1..5 (and
-// within 0.3 us at T = 6..8), the arithmetic being a small part of a
-// latency-bound read.
+// Why not MFMA: the T <= 8 tokens of the pages' windows fill at most half of a
+// 16-wide MFMA tile, and on MI355X the two-kernel read was measured ~1.5 us
+// slower with v_mfma_f32_16x16x32_bf16 tiles than with this VALU path at
+// T = 1..5 (and within 0.3 us at T = 6..8), the arithmetic being a small part
+// of a latency-bound read.
+//
+// T = 9..16: the down kernel takes the tokens in groups of 8 (the next
+// group's x loads overlap the current group's FMAs); the up kernel streams
+// each token's activations from LDS, so both keep their T <= 8 structure.
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
@@ -127,16 +131,26 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restri
   const int ca = 512 * wave + 8 * lane;         // 8 columns: one 16-byte chunk per row
   const int cb = 2048 + 128 * wave + 2 * lane;  // 2 columns: one dword per row
 
-  // 1. x and w_norm first (vector loads complete in issue order), then the 5 weight rows
-  f32x4 xa0[T], xa1[T];
-  f32x2 xb[T];
+  // Tokens are taken in groups of up to 8 (x of one group in registers at a time).
+  constexpr int TG = T < 8 ? T : 8;
+  constexpr int NG = (T + TG - 1) / TG;
+  f32x4 xa0[TG], xa1[TG];
+  f32x2 xb[TG];
+  auto load_x = [&](int grp) {
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const float* xt = x + ((size_t)t * S + s) * D;
-    xa0[t] = ld4(xt + ca);
-    xa1[t] = ld4(xt + ca + 4);
-    xb[t] = ld2(xt + cb);
-  }
+    for (int i = 0; i < TG; ++i) {
+      const int t = grp * TG + i;
+      if (t < T) {
+        const float* xt = x + ((size_t)t * S + s) * D;
+        xa0[i] = ld4(xt + ca);
+        xa1[i] = ld4(xt + ca + 4);
+        xb[i] = ld2(xt + cb);
+      }
+    }
+  };
+
+  // 1. x of the first group and w_norm first (vector loads complete in issue order), then the 5 weight rows
+  load_x(0);
   const float* ns = w_norm + s * D;
   const f32x4 na0 = ld4(ns + ca), na1 = ld4(ns + ca + 4);
   const f32x2 nb = ld2(ns + cb);
@@ -150,47 +164,59 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restri
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. activations x*w_norm (unscaled) and the lane's sums of squares
   constexpr int N = round4((DOWN_ROWS + 1) * T);
-  float act[T][10];
   float v[N];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      act[t][e] = xa0[t][e] * na0[e];
-      act[t][4 + e] = xa1[t][e] * na1[e];
-    }
-    act[t][8] = xb[t][0] * nb[0];
-    act[t][9] = xb[t][1] * nb[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa0[t][e], xa0[t][e], ss);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa1[t][e], xa1[t][e], ss);
-    ss = __builtin_fmaf(xb[t][0], xb[t][0], ss);
-    ss = __builtin_fmaf(xb[t][1], xb[t][1], ss);
-    v[DOWN_ROWS * T + t] = ss;
-  }
-#pragma unroll
   for (int i = (DOWN_ROWS + 1) * T; i < N; ++i) v[i] = 0.f;
-
-  // 3. per row: the BF16 weights widened exactly to FP32, one FMA chain per token
 #pragma unroll
-  for (int r = 0; r < DOWN_ROWS; ++r) {
-    const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
-    float wv[10];
+  for (int grp = 0; grp < NG; ++grp) {
+    // 2. activations x*w_norm (unscaled) and the lane's sums of squares of this group's tokens
+    float act[TG][10];
 #pragma unroll
-    for (int e = 0; e < 5; ++e) {
-      wv[2 * e] = __uint_as_float(u[e] << 16);
-      wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    for (int i = 0; i < TG; ++i) {
+      const int t = grp * TG + i;
+      if (t < T) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          act[i][e] = xa0[i][e] * na0[e];
+          act[i][4 + e] = xa1[i][e] * na1[e];
+        }
+        act[i][8] = xb[i][0] * nb[0];
+        act[i][9] = xb[i][1] * nb[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa0[i][e], xa0[i][e], ss);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa1[i][e], xa1[i][e], ss);
+        ss = __builtin_fmaf(xb[i][0], xb[i][0], ss);
+        ss = __builtin_fmaf(xb[i][1], xb[i][1], ss);
+        v[DOWN_ROWS * T + t] = ss;
+      }
     }
+    if (grp + 1 < NG) {  // the next group's x streams in while this group computes
+      load_x(grp + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 3. per row: the BF16 weights widened exactly to FP32, one FMA chain per token
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float a = 0.f;
+    for (int r = 0; r < DOWN_ROWS; ++r) {
+      const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
+      float wv[10];
 #pragma unroll
-      for (int e = 0; e < 10; ++e) a = __builtin_fmaf(wv[e], act[t][e], a);
-      v[r * T + t] = a;
+      for (int e = 0; e < 5; ++e) {
+        wv[2 * e] = __uint_as_float(u[e] << 16);
+        wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < TG; ++i) {
+        const int t = grp * TG + i;
+        if (t < T) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 10; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
+          v[r * T + t] = acc;
+        }
+      }
     }
   }
 
@@ -291,11 +317,11 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  __shared__ __attribute__((aligned(16))) float lo_sm[TMAX * R];
-  __shared__ uint4 acta_sm[2][TMAX][32];  // K [8q, 8q+8): high, low parts
-  __shared__ uint2 actb_sm[TMAX][32];     // K [256+2q, +2): (high, low)
-  __shared__ float gate_sm[TMAX][S];
-  __shared__ float u_sm[TMAX][UP_ROWS];
+  __shared__ __attribute__((aligned(16))) float lo_sm[T * R];
+  __shared__ uint4 acta_sm[2][T][32];  // K [8q, 8q+8): high, low parts
+  __shared__ uint2 actb_sm[T][32];     // K [256+2q, +2): (high, low)
+  __shared__ float gate_sm[T][S];
+  __shared__ float u_sm[T][UP_ROWS];
 
   // 3. lo[t][k] = ((p0 + p1) + p2) + p3 (+ inj)
 #pragma unroll
@@ -310,8 +336,8 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
   }
   __syncthreads();
   // 4. lo as BF16 high/low v_dot2 operands, in each lane's K order; gates; lo for inspection
-  if (tid < T * 32) {
-    const int t = tid >> 5, qq = tid & 31;
+  for (int i = tid; i < T * 32; i += UP_THREADS) {
+    const int t = i >> 5, qq = i & 31;
     float va[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) va[e] = lo_sm[t * R + 8 * qq + e];
@@ -389,11 +415,14 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
 typedef void (*down_fn)(const uint16_t*, const float*, const float*, float*, float*);
 typedef void (*up_fn)(const uint4*, const float*, const float*, const float*, float*, float*, float*);
 
-static const down_fn kDown[TMAX] = {hc_down<1>, hc_down<2>, hc_down<3>, hc_down<4>,
-                                    hc_down<5>, hc_down<6>, hc_down<7>, hc_down<8>};
+static const down_fn kDown[TMAX] = {hc_down<1>,  hc_down<2>,  hc_down<3>,  hc_down<4>,  hc_down<5>,  hc_down<6>,
+                                    hc_down<7>,  hc_down<8>,  hc_down<9>,  hc_down<10>, hc_down<11>, hc_down<12>,
+                                    hc_down<13>, hc_down<14>, hc_down<15>, hc_down<16>};
 #define HCR_UP_ROW(T) {{hc_up<T, false, false>, hc_up<T, false, true>}, {hc_up<T, true, false>, hc_up<T, true, true>}}
-static const up_fn kUp[TMAX][2][2] = {HCR_UP_ROW(1), HCR_UP_ROW(2), HCR_UP_ROW(3), HCR_UP_ROW(4),
-                                      HCR_UP_ROW(5), HCR_UP_ROW(6), HCR_UP_ROW(7), HCR_UP_ROW(8)};
+static const up_fn kUp[TMAX][2][2] = {HCR_UP_ROW(1),  HCR_UP_ROW(2),  HCR_UP_ROW(3),  HCR_UP_ROW(4),
+                                      HCR_UP_ROW(5),  HCR_UP_ROW(6),  HCR_UP_ROW(7),  HCR_UP_ROW(8),
+                                      HCR_UP_ROW(9),  HCR_UP_ROW(10), HCR_UP_ROW(11), HCR_UP_ROW(12),
+                                      HCR_UP_ROW(13), HCR_UP_ROW(14), HCR_UP_ROW(15), HCR_UP_ROW(16)};
 #undef HCR_UP_ROW
 
 int launch_read(int T, const void* w_down, const void* w_up, const float* w_norm, void* scratch,

@@ -27,7 +27,8 @@ import numpy as np
 S_STREAMS = 4
 D_STREAM = 2560
 R_DOWN = 320
-T_MAX = 8
+T_MAX = 8       # largest verify window the pages measure
+T_WIDE = 16     # larger windows, also generated
 
 # purposes (second element of a seed key)
 _P_WDOWN, _P_WUP, _P_WNORM, _P_X, _P_PENDING, _P_INJ, _P_NEARDUP = range(1, 8)

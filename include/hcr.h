@@ -17,6 +17,7 @@
  *   out[t,s,c] = pending[t,s,c] (or 0) + sigmoid(lo[t,s]) * u[t, s*d+c]
  *   mean[t,c]  = (1/4) * sum_s out[t,s,c]
  *
+ * T may be 0..16 (the pages' windows are 1..8 tokens; 9..16 serve larger windows).
  * Arithmetic is FP32 (BF16 weights are widened exactly); summation orders
  * are fixed, so a call is bitwise reproducible, also as a replayed HIP graph.
  *
@@ -48,7 +49,7 @@ extern "C" {
 #define HCR_STREAMS 4      /* residual streams S */
 #define HCR_STREAM_D 2560  /* values per stream d */
 #define HCR_RANK 320       /* down-projection rows R (up-projection K) */
-#define HCR_T_MAX 8        /* tokens per read */
+#define HCR_T_MAX 16       /* tokens per read */
 
 enum {
   HCR_OK = 0,

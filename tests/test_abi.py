@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_geometry_and_scratch(lib):
-    assert hcr.hcr_geometry() == (4, 2560, 320, 8)
+    assert hcr.hcr_geometry() == (4, 2560, 320, 16)
     n = hcr.hcr_scratch_bytes()
     lo, rs = hcr.hcr_scratch_layout()
     assert n % 256 == 0 and lo % 256 == 0 and rs % 256 == 0
@@ -72,7 +72,7 @@ T_BYTES = 4 * 2560 * 4
 
 
 @pytest.mark.parametrize("T,args,rc", [
-    (9, {}, hcr.HCR_EINVAL),
+    (17, {}, hcr.HCR_EINVAL),
     (-1, {}, hcr.HCR_EINVAL),
     (2, dict(x=None), hcr.HCR_EINVAL),
     (2, dict(out=None), hcr.HCR_EINVAL),

@@ -35,11 +35,11 @@ def _read(reader, x, p, inj):
     return out, mean
 
 
-@pytest.mark.parametrize("T", range(1, 9))
+@pytest.mark.parametrize("T", range(1, gen.T_WIDE + 1))
 @pytest.mark.parametrize("with_pending", [False, True])
 @pytest.mark.parametrize("with_inj", [False, True])
 def test_matrix(wset, T, with_pending, with_inj):
-    """T = 1..8 x pending write on/off x injection on/off (32 cases), one weight set."""
+    """T = 1..16 x pending write on/off x injection on/off (64 cases), one weight set."""
     w, reader = wset
     x = gen.activations(1, T, index=T)
     p = gen.pending(1, T, index=T) if with_pending else None
@@ -79,6 +79,17 @@ def test_numerics_stress_32_sets():
         errs = check_read(r, 8, out, mean, ref, f"stress set {k}")
         worst = max(worst, max(errs.values()))
     print(f"numerics stress: worst error {worst:.3e} of max |ref|")
+
+
+@pytest.mark.parametrize("T", [9, 12, 16])
+def test_numerics_stress_wide_windows(T):
+    """Windows beyond 8 tokens (two token groups in the down kernel) under the stress inputs, 4 weight sets."""
+    c = gen.numerics_stress(6, T=T, n_sets=4)
+    for k, w in enumerate(c["weights"]):
+        r = reader_for(w)
+        out, mean = _read(r, c["x"][k], c["pending"][k], c["inj"][k])
+        ref = oracle.hc_read(c["x"][k], w.w_norm, w.w_down, w.w_up, pending=c["pending"][k], inj=c["inj"][k])
+        check_read(r, T, out, mean, ref, f"wide stress T={T} set {k}")
 
 
 def test_cold_rotation_all_sets_all_T():
@@ -173,10 +184,10 @@ def test_repeated_reads_bitwise(wset):
     assert torch.equal(o, o0) and torch.equal(m, m0)
 
 
-def test_token_results_do_not_depend_on_T(wset):
-    """Each token's result is the same, bit for bit, whether it is read alone or in a window of 8."""
+@pytest.mark.parametrize("T", [8, 16])
+def test_token_results_do_not_depend_on_T(wset, T):
+    """Each token's result is the same, bit for bit, whether it is read alone or in a window of T."""
     w, reader = wset
-    T = 8
     x, p, inj = gen.activations(8, T), gen.pending(8, T), gen.injection(8, T)
     o8, m8 = _read(reader, x, p, inj)
     o8, m8 = o8.clone(), m8.clone()
@@ -216,7 +227,7 @@ def test_numerics_stress_graph_replay_bitwise():
             assert torch.equal(outs[k], o) and torch.equal(means[k], m), f"replay {rep} read {k}"
 
 
-@pytest.mark.parametrize("T", [1, 6, 8])
+@pytest.mark.parametrize("T", [1, 6, 8, 9, 16])
 def test_graph_replay_bitwise(wset, T):
     """A captured read replayed several times (with eager work between) equals the direct call, bitwise."""
     w, reader = wset
