@@ -31,7 +31,7 @@ T_MAX = 8       # largest verify window the pages measure
 T_WIDE = 16     # larger windows, also generated
 
 # purposes (second element of a seed key)
-_P_WDOWN, _P_WUP, _P_WNORM, _P_X, _P_PENDING, _P_INJ, _P_NEARDUP = range(1, 8)
+_P_WDOWN, _P_WUP, _P_WNORM, _P_X, _P_PENDING, _P_INJ, _P_NEARDUP, _P_EDGE = range(1, 9)
 
 
 def rng(*key):
@@ -133,6 +133,61 @@ def with_near_duplicate_rows(w_down_bits, base, index=0, frac_rows=0.01,
         row[cols] = (row[cols] & 0x8000) | (mag + step)
         w[tr] = row.astype(np.uint16)
     return w, np.sort(targets)
+
+
+Q8_BLOCK = 32  # weights per block of the Q8_0 copies (along a row)
+Q8_EDGE_FAMILIES = ("normal", "zero", "one_nonzero", "half_integers_amax_127", "tiny", "large", "huge",
+                    "negative_amax", "opposite_amax", "multiples_of_2^-7")
+
+
+def q8_edge_weights(base, rows=64, K=1024, index=0):
+    """BF16 bits [rows][K] whose 32-weight blocks cycle through ``Q8_EDGE_FAMILIES``.
+
+    Block b (row-major over the rows' blocks) has family b mod 10: N(0, 0.02);
+    all zero; one nonzero entry; half-integers +-0.5 .. +-126.5 with one +-127
+    (a block maximum of 127 puts every entry on a rounding tie); N(0, 1e-7);
+    N(0, 1e4); N(0, 1e7); N(0, 0.02) with its largest magnitude made negative;
+    two entries +A and -A as the largest magnitudes; integers -127..127 times
+    2**-7 with one +-127.  Every value is drawn in float32 and stored as BF16.
+    """
+    if K % Q8_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    g = rng(base, _P_EDGE, index)
+    nb = rows * K // Q8_BLOCK
+    w = np.zeros((nb, Q8_BLOCK), dtype=np.float32)
+    for b in range(nb):
+        fam = b % len(Q8_EDGE_FAMILIES)
+        z = g.standard_normal(Q8_BLOCK).astype(np.float32)
+        if fam == 0:
+            w[b] = 0.02 * z
+        elif fam == 2:
+            w[b, int(g.integers(0, Q8_BLOCK))] = np.float32(g.standard_normal() * 0.05)
+        elif fam == 3:
+            v = g.integers(-127, 127, size=Q8_BLOCK).astype(np.float32) + np.float32(0.5)
+            v[int(g.integers(0, Q8_BLOCK))] = np.float32(127.0 if g.integers(0, 2) else -127.0)
+            w[b] = v
+        elif fam == 4:
+            w[b] = np.float32(1e-7) * z
+        elif fam == 5:
+            w[b] = np.float32(1e4) * z
+        elif fam == 6:
+            w[b] = np.float32(1e7) * z
+        elif fam == 7:
+            v = 0.02 * z
+            i = int(np.argmax(np.abs(v)))
+            v[i] = -np.abs(v[i]) * np.float32(1.5)
+            w[b] = v
+        elif fam == 8:
+            v = 0.01 * z
+            i, j = g.choice(Q8_BLOCK, size=2, replace=False)
+            a = np.float32(np.max(np.abs(v)) * 2.0 + 0.01)
+            v[i], v[j] = a, -a
+            w[b] = v
+        elif fam == 9:
+            v = g.integers(-127, 128, size=Q8_BLOCK).astype(np.float32)
+            v[int(g.integers(0, Q8_BLOCK))] = np.float32(127.0 if g.integers(0, 2) else -127.0)
+            w[b] = v * np.float32(2.0 ** -7)
+    return f32_to_bf16_bits(w.reshape(rows, K))
 
 
 # ---------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-"""FP64 CPU reference ("oracle") of the BF16 hyper-connection read.
+"""FP64 CPU reference ("oracle") of the BF16 hyper-connection read and of its Q8_0 sibling.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
@@ -12,6 +12,8 @@ from .reference import (  # noqa: F401
     down_projection,
     epilogue,
     hc_read,
+    hc_read_decoded,
     stream_rms_scale,
     up_projection,
 )
+from .q8_0 import dequantize_q8_0, hc_read_q8_0, quantize_q8_0  # noqa: F401,E402

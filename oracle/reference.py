@@ -130,10 +130,17 @@ def hc_read(x, w_norm, w_down_bits, w_up_bits, pending=None, inj=None, eps=EPS):
     w_up_bits: uint16 [S*d][R], pending: [T][S][d] or None, inj: [T][R] or None.
     Returns a dict with out [T][S][d], mean [T][d], lo [T][R], rs [T][S], u [T][S*d].
     """
+    return hc_read_decoded(x, w_norm, bf16_bits_to_f64(w_down_bits), bf16_bits_to_f64(w_up_bits),
+                           pending=pending, inj=inj, eps=eps)
+
+
+def hc_read_decoded(x, w_norm, w_down, w_up, pending=None, inj=None, eps=EPS):
+    """The same read on weights already decoded to float64 (any storage format).
+
+    w_down: [R][S*d] float64, w_up: [S*d][R] float64; the rest as ``hc_read``.
+    """
     x = np.asarray(x, dtype=np.float64)
     T, S, d = x.shape
-    w_down = bf16_bits_to_f64(w_down_bits)
-    w_up = bf16_bits_to_f64(w_up_bits)
     R = w_down.shape[0]
     if w_down.shape != (R, S * d) or w_up.shape != (S * d, R):
         raise ValueError("weight shapes do not match x")

@@ -59,3 +59,12 @@ def test_near_duplicate_rows():
         delta = wd[tr].astype(np.int32) - w.w_down[src].astype(np.int32)
         assert set(np.unique(np.abs(delta))) <= {0, 1}
         assert np.array_equal(wd[tr] & 0x8000, w.w_down[src] & 0x8000)
+
+
+def test_q8_edge_weights_are_seeded_and_cover_every_family():
+    a, b = gen.q8_edge_weights(3), gen.q8_edge_weights(3)
+    assert np.array_equal(a, b) and a.dtype == np.uint16 and a.shape == (64, 1024)
+    blocks = a.reshape(-1, 32)
+    assert not np.any(blocks[1::10])                               # the all-zero family
+    assert np.all(np.count_nonzero(blocks[2::10], axis=1) == 1)   # one nonzero entry
+    assert not np.array_equal(a, gen.q8_edge_weights(4))
