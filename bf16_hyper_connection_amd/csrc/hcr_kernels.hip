@@ -1,4 +1,5 @@
-// HIP kernels of the BF16 hyper-connection read for gfx950 (MI355X).
+// HIP kernels of the BF16 hyper-connection read for gfx950 (MI355X), and of
+// its sibling on Q8_0 copies of the two projections.
 //
 // The read (Strata PR #2812, two-kernel BF16 hyper-connection read, What
 // changed; Strata PR #2070, Turing hyper-connection read kernels) is split in
@@ -47,6 +48,19 @@
 // its small inputs first (x, w_norm; partials, injection, pending) and its
 // weight tile after them, all before any arithmetic.
 //
+// Q8_0 copies (Strata PR #2812, Summary: the sibling read of #2810 on Q8_0
+// copies of the projections; the block is read as GGML's Q8_0: 32 weights of
+// a row share one binary16 scale d, each weight is d times an int8 code).
+// The same two kernels, templated on the weight format, read int8 codes (8 +
+// 2 per lane and row, half the bytes of BF16) and two scales per lane and
+// row; a lane's 8-column chunk and its 2-column chunk each sit inside one
+// block, so the lane multiplies each chunk's FMA sum by its block's scale.
+// The up kernel takes lo in FP32 from LDS (no BF16 split): the codes widen
+// exactly to FP32.  q8_quantize makes the copies on the device: 4 lanes per
+// block, the block maximum over the quad by DPP, then d = amax / 127,
+// codes = round(w * (1 / d)) with ties away from zero, all in IEEE binary32,
+// and d stored rounded to binary16.
+//
 // Determinism: every sum has a fixed order, so repeated calls and graph
 // replays are bitwise identical, and each token's result does not depend on T.
 
@@ -58,6 +72,15 @@
 namespace hcr {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// byte k of u as a signed 8-bit code, widened exactly to FP32
+__device__ __forceinline__ float code(uint32_t u, int k) {
+  return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(u >> (8 * k))));
+}
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -119,8 +142,9 @@ __device__ __forceinline__ void wave_sum(float (&v)[N]) {
 constexpr int round4(int n) { return (n + 3) & ~3; }
 
 // down: one stream x 5 rows per work-group; rs applied here (the work-group sees the whole stream)
-template <int T>
-__global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restrict__ w_down,
+template <int T, int FMT>
+__global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__ w_down,
+                                                           const uint16_t* __restrict__ s_down,
                                                            const float* __restrict__ x,
                                                            const float* __restrict__ w_norm,
                                                            float* __restrict__ part, float* __restrict__ rs_out) {
@@ -154,13 +178,27 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restri
   const float* ns = w_norm + s * D;
   const f32x4 na0 = ld4(ns + ca), na1 = ld4(ns + ca + 4);
   const f32x2 nb = ld2(ns + cb);
-  const uint16_t* wr = w_down + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
-  uint4 wa[DOWN_ROWS];
-  uint32_t wb[DOWN_ROWS];
+  uint4 wa[DOWN_ROWS];      // BF16: 8 weights at ca
+  uint32_t wb[DOWN_ROWS];   // BF16: 2 weights at cb; Q8_0: 2 codes at cb
+  uint2 qa[DOWN_ROWS];      // Q8_0: 8 codes at ca
+  uint32_t sa[DOWN_ROWS], sb[DOWN_ROWS];  // Q8_0: scales of the blocks holding ca and cb
+  if constexpr (FMT == FMT_BF16) {
+    const uint16_t* wr = static_cast<const uint16_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
 #pragma unroll
-  for (int r = 0; r < DOWN_ROWS; ++r) {
-    wa[r] = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
-    wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+    for (int r = 0; r < DOWN_ROWS; ++r) {
+      wa[r] = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
+      wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+    }
+  } else {
+    const int8_t* wr = static_cast<const int8_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
+    const uint16_t* sr = s_down + (size_t)(DOWN_ROWS * g) * (DD / Q8_BLOCK) + (size_t)s * (D / Q8_BLOCK);
+#pragma unroll
+    for (int r = 0; r < DOWN_ROWS; ++r) {
+      qa[r] = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
+      wb[r] = *reinterpret_cast<const uint16_t*>(wr + (size_t)r * DD + cb);
+      sa[r] = sr[(size_t)r * (DD / Q8_BLOCK) + ca / Q8_BLOCK];
+      sb[r] = sr[(size_t)r * (DD / Q8_BLOCK) + cb / Q8_BLOCK];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -197,24 +235,43 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const uint16_t* __restri
       load_x(grp + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // 3. per row: the BF16 weights widened exactly to FP32, one FMA chain per token
+    // 3. per row: the weights widened exactly to FP32, one FMA chain per token
+    //    (Q8_0: one chain per block chunk, each times its block's scale)
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
-      const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
       float wv[10];
+      if constexpr (FMT == FMT_BF16) {
+        const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
 #pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        wv[2 * e] = __uint_as_float(u[e] << 16);
-        wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        for (int e = 0; e < 5; ++e) {
+          wv[2 * e] = __uint_as_float(u[e] << 16);
+          wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[e] = code(qa[r].x, e);
+          wv[4 + e] = code(qa[r].y, e);
+        }
+        wv[8] = code(wb[r], 0);
+        wv[9] = code(wb[r], 1);
       }
 #pragma unroll
       for (int i = 0; i < TG; ++i) {
         const int t = grp * TG + i;
         if (t < T) {
-          float acc = 0.f;
+          if constexpr (FMT == FMT_BF16) {
+            float acc = 0.f;
 #pragma unroll
-          for (int e = 0; e < 10; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
-          v[r * T + t] = acc;
+            for (int e = 0; e < 10; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
+            v[r * T + t] = acc;
+          } else {
+            float a8 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a8 = __builtin_fmaf(wv[e], act[i][e], a8);
+            const float a2 = __builtin_fmaf(wv[9], act[i][9], wv[8] * act[i][8]);
+            v[r * T + t] = __builtin_fmaf(half_bits_to_float(sa[r]), a8, half_bits_to_float(sb[r]) * a2);
+          }
         }
       }
     }
@@ -265,8 +322,9 @@ __device__ __forceinline__ void half_wave_sum(float (&v)[N]) {
 constexpr int round2(int n) { return (n + 1) & ~1; }
 
 // up: lo = sum of the 4 stream partials (+ injection); 40 rows of W_up (10 columns x 4 streams) per work-group
-template <int T, bool INJ, bool PEND>
-__global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_up,
+template <int T, bool INJ, bool PEND, int FMT>
+__global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_up,
+                                                         const uint16_t* __restrict__ s_up,
                                                          const float* __restrict__ part,
                                                          const float* __restrict__ inj, const float* pending,
                                                          float* out, float* __restrict__ mean,
@@ -305,21 +363,32 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
 
   // 2. weights: iteration m, half h -> row rw = 10*wave + 2m + h (column rw >> 2, stream rw & 3);
   //    lane q owns K [8q, 8q+8) (one 16-byte chunk) and [256 + 2q, 256 + 2q + 2) (one dword)
-  uint4 wa[UP_ITERS];
-  uint32_t wb[UP_ITERS];
-  const uint16_t* wu16 = reinterpret_cast<const uint16_t*>(w_up);
+  uint4 wa[UP_ITERS];     // BF16: K [8q, 8q+8)
+  uint32_t wb[UP_ITERS];  // BF16: K [256+2q, +2); Q8_0: the 2 codes there
+  uint2 qa[UP_ITERS];     // Q8_0: codes at K [8q, 8q+8)
+  uint32_t sa[UP_ITERS], sb[UP_ITERS];  // Q8_0: scales of blocks q/4 and 8 + q/16 of the row
 #pragma unroll
   for (int m = 0; m < UP_ITERS; ++m) {
     const int rw = UP_WAVE_ROWS * wave + 2 * m + h;
-    const uint16_t* row = wu16 + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
-    wa[m] = *reinterpret_cast<const uint4*>(row + 8 * q);
-    wb[m] = *reinterpret_cast<const uint32_t*>(row + 256 + 2 * q);
+    const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+    if constexpr (FMT == FMT_BF16) {
+      const uint16_t* row = static_cast<const uint16_t*>(w_up) + j * R;
+      wa[m] = *reinterpret_cast<const uint4*>(row + 8 * q);
+      wb[m] = *reinterpret_cast<const uint32_t*>(row + 256 + 2 * q);
+    } else {
+      const int8_t* row = static_cast<const int8_t*>(w_up) + j * R;
+      qa[m] = *reinterpret_cast<const uint2*>(row + 8 * q);
+      wb[m] = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * q);
+      sa[m] = s_up[j * (R / Q8_BLOCK) + q / 4];
+      sb[m] = s_up[j * (R / Q8_BLOCK) + 8 + q / 16];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   __shared__ __attribute__((aligned(16))) float lo_sm[T * R];
-  __shared__ uint4 acta_sm[2][T][32];  // K [8q, 8q+8): high, low parts
-  __shared__ uint2 actb_sm[T][32];     // K [256+2q, +2): (high, low)
+  constexpr int TS = FMT == FMT_BF16 ? T : 1;  // the BF16 split of lo; Q8_0 reads lo itself
+  __shared__ uint4 acta_sm[2][TS][32];  // K [8q, 8q+8): high, low parts
+  __shared__ uint2 actb_sm[TS][32];     // K [256+2q, +2): (high, low)
   __shared__ float gate_sm[T][S];
   __shared__ float u_sm[T][UP_ROWS];
 
@@ -336,7 +405,7 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
   }
   __syncthreads();
   // 4. lo as BF16 high/low v_dot2 operands, in each lane's K order; gates; lo for inspection
-  for (int i = tid; i < T * 32; i += UP_THREADS) {
+  for (int i = tid; FMT == FMT_BF16 && i < T * 32; i += UP_THREADS) {
     const int t = i >> 5, qq = i & 31;
     float va[8];
 #pragma unroll
@@ -356,12 +425,43 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
   __syncthreads();
 
   // 5. dot products: per (iteration, token) the lane's 10 K values, high then low part of lo
+  //    (Q8_0: FP32 lo times the widened codes, one chain per block chunk, times its scale)
   constexpr int N = round2(UP_ITERS * T);
   float v[N];
 #pragma unroll
   for (int i = UP_ITERS * T; i < N; ++i) v[i] = 0.f;
+  if constexpr (FMT == FMT_Q8_0) {
+    float wv[UP_ITERS][10], da[UP_ITERS], db[UP_ITERS];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
+    for (int m = 0; m < UP_ITERS; ++m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wv[m][e] = code(qa[m].x, e);
+        wv[m][4 + e] = code(qa[m].y, e);
+      }
+      wv[m][8] = code(wb[m], 0);
+      wv[m][9] = code(wb[m], 1);
+      da[m] = half_bits_to_float(sa[m]);
+      db[m] = half_bits_to_float(sb[m]);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lo_sm + t * R + 8 * q);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lo_sm + t * R + 8 * q + 4);
+      const f32x2 l2 = *reinterpret_cast<const f32x2*>(lo_sm + t * R + 256 + 2 * q);
+      const float lv[10] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3], l2[0], l2[1]};
+#pragma unroll
+      for (int m = 0; m < UP_ITERS; ++m) {
+        float a8 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8 = __builtin_fmaf(wv[m][e], lv[e], a8);
+        const float a2 = __builtin_fmaf(wv[m][9], lv[9], wv[m][8] * lv[8]);
+        v[m * T + t] = __builtin_fmaf(da[m], a8, db[m] * a2);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < (FMT == FMT_BF16 ? T : 0); ++t) {
     const uint4 ah = acta_sm[0][t][q], al = acta_sm[1][t][q];
     const uint2 ab = actb_sm[t][q];
     const uint32_t hh[5] = {ah.x, ah.y, ah.z, ah.w, ab.x};
@@ -410,34 +510,84 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const uint4* __restrict__ w_
 }
 
 // ---------------------------------------------------------------------------
+// Q8_0 copies on the device: 4 lanes per 32-weight block (8 BF16 weights each)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void q8_quantize(const uint4* __restrict__ w, size_t n_blocks,
+                                                   uint2* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // chunk i = block i/4, weights 8(i%4) ..
+  const bool ok = (i >> 2) < n_blocks;                       // a quad is entirely in or out
+  const uint4 u = ok ? w[i] : make_uint4(0, 0, 0, 0);
+  const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(uu[e] << 16);
+    f[2 * e + 1] = __uint_as_float(uu[e] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  amax = fmaxf(amax, dpp<0xB1>(amax));  // quad_perm [1,0,3,2]
+  amax = fmaxf(amax, dpp<0x4E>(amax));  // quad_perm [2,3,0,1]
+  const float d = amax / 127.0f;        // IEEE binary32 division (correctly rounded)
+  const float id = d != 0.f ? 1.0f / d : 0.f;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int qv = static_cast<int>(__builtin_roundf(f[e] * id));  // ties away from zero
+    packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * (e & 3));
+  }
+  if (ok) {
+    codes[i] = make_uint2(packed[0], packed[1]);
+    if ((i & 3) == 0) scales[i >> 2] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d));
+  }
+}
+
+int launch_quantize_q8_0(const void* w, size_t n_blocks, void* codes, void* scales, void* stream) {
+  const size_t threads = n_blocks * 4;
+  const size_t wgs = (threads + 255) / 256;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(q8_quantize, dim3(static_cast<unsigned>(wgs)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint4*>(w), n_blocks,
+                     static_cast<uint2*>(codes), static_cast<uint16_t*>(scales));
+  return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-typedef void (*down_fn)(const uint16_t*, const float*, const float*, float*, float*);
-typedef void (*up_fn)(const uint4*, const float*, const float*, const float*, float*, float*, float*);
+typedef void (*down_fn)(const void*, const uint16_t*, const float*, const float*, float*, float*);
+typedef void (*up_fn)(const void*, const uint16_t*, const float*, const float*, const float*, float*, float*,
+                      float*);
 
-static const down_fn kDown[TMAX] = {hc_down<1>,  hc_down<2>,  hc_down<3>,  hc_down<4>,  hc_down<5>,  hc_down<6>,
-                                    hc_down<7>,  hc_down<8>,  hc_down<9>,  hc_down<10>, hc_down<11>, hc_down<12>,
-                                    hc_down<13>, hc_down<14>, hc_down<15>, hc_down<16>};
-#define HCR_UP_ROW(T) {{hc_up<T, false, false>, hc_up<T, false, true>}, {hc_up<T, true, false>, hc_up<T, true, true>}}
-static const up_fn kUp[TMAX][2][2] = {HCR_UP_ROW(1),  HCR_UP_ROW(2),  HCR_UP_ROW(3),  HCR_UP_ROW(4),
-                                      HCR_UP_ROW(5),  HCR_UP_ROW(6),  HCR_UP_ROW(7),  HCR_UP_ROW(8),
-                                      HCR_UP_ROW(9),  HCR_UP_ROW(10), HCR_UP_ROW(11), HCR_UP_ROW(12),
-                                      HCR_UP_ROW(13), HCR_UP_ROW(14), HCR_UP_ROW(15), HCR_UP_ROW(16)};
+#define HCR_DOWN_ROW(F) \
+  {hc_down<1, F>,  hc_down<2, F>,  hc_down<3, F>,  hc_down<4, F>,  hc_down<5, F>,  hc_down<6, F>,  \
+   hc_down<7, F>,  hc_down<8, F>,  hc_down<9, F>,  hc_down<10, F>, hc_down<11, F>, hc_down<12, F>, \
+   hc_down<13, F>, hc_down<14, F>, hc_down<15, F>, hc_down<16, F>}
+static const down_fn kDown[2][TMAX] = {HCR_DOWN_ROW(FMT_BF16), HCR_DOWN_ROW(FMT_Q8_0)};
+#undef HCR_DOWN_ROW
+#define HCR_UP_T(T, F) {{hc_up<T, false, false, F>, hc_up<T, false, true, F>}, {hc_up<T, true, false, F>, hc_up<T, true, true, F>}}
+#define HCR_UP_ROW(F)                                                                              \
+  {HCR_UP_T(1, F),  HCR_UP_T(2, F),  HCR_UP_T(3, F),  HCR_UP_T(4, F),  HCR_UP_T(5, F),  HCR_UP_T(6, F),  \
+   HCR_UP_T(7, F),  HCR_UP_T(8, F),  HCR_UP_T(9, F),  HCR_UP_T(10, F), HCR_UP_T(11, F), HCR_UP_T(12, F), \
+   HCR_UP_T(13, F), HCR_UP_T(14, F), HCR_UP_T(15, F), HCR_UP_T(16, F)}
+static const up_fn kUp[2][TMAX][2][2] = {HCR_UP_ROW(FMT_BF16), HCR_UP_ROW(FMT_Q8_0)};
 #undef HCR_UP_ROW
+#undef HCR_UP_T
 
-int launch_read(int T, const void* w_down, const void* w_up, const float* w_norm, void* scratch,
-                const float* x, const float* pending, const float* inj, float* out, float* mean,
-                void* stream) {
+int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, const void* w_up, const uint16_t* s_up,
+                const float* w_norm, void* scratch, const float* x, const float* pending, const float* inj,
+                float* out, float* mean, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* sc = static_cast<char*>(scratch);
   float* part = reinterpret_cast<float*>(sc + OFF_PART);
   float* lo = reinterpret_cast<float*>(sc + OFF_LO);
   float* rs = reinterpret_cast<float*>(sc + OFF_RS);
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
-  hipLaunchKernelGGL(kDown[T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, static_cast<const uint16_t*>(w_down),
-                     x, w_norm, part, rs);
-  hipLaunchKernelGGL(kUp[T - 1][inj != nullptr][pending != nullptr], dim3(UP_WGS), dim3(UP_THREADS), 0, st,
-                     static_cast<const uint4*>(w_up), part, inj, pending, out, mean, lo);
+  hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, w_down, s_down, x, w_norm, part,
+                     rs);
+  hipLaunchKernelGGL(kUp[fmt][T - 1][inj != nullptr][pending != nullptr], dim3(UP_WGS), dim3(UP_THREADS), 0, st,
+                     w_up, s_up, part, inj, pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }
 

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include "hcr.h"
 
@@ -38,9 +39,19 @@ constexpr size_t SCRATCH_BYTES = align256(OFF_RS + size_t(TMAX) * S * 4);
 static_assert(S == 4 && D == 4 * 512 + 4 * 128 && R % DOWN_ROWS == 0, "down tiling must divide the geometry");
 static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0, "up tiling must divide the geometry");
 
-// Enqueue the two kernels of one read (T in 1..TMAX; arguments already validated).
-int launch_read(int T, const void* w_down, const void* w_up, const float* w_norm, void* scratch,
-                const float* x, const float* pending, const float* inj, float* out, float* mean,
-                void* stream);
+// ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
+enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
+constexpr int Q8_BLOCK = 32;
+static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0,
+              "a lane's 8- and 2-weight chunks must each sit inside one Q8_0 block");
+
+// Enqueue the two kernels of one read (T in 1..TMAX; arguments already validated).  For
+// FMT_BF16 the scale pointers are unused.
+int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, const void* w_up, const uint16_t* s_up,
+                const float* w_norm, void* scratch, const float* x, const float* pending, const float* inj,
+                float* out, float* mean, void* stream);
+
+// Enqueue the Q8_0 quantisation of n_blocks 32-weight blocks (arguments already validated).
+int launch_quantize_q8_0(const void* w, size_t n_blocks, void* codes, void* scales, void* stream);
 
 }  // namespace hcr

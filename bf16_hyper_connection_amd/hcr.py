@@ -1,4 +1,4 @@
-"""ctypes binding of libhcr.so, the BF16 hyper-connection read (C ABI in include/hcr.h).
+"""ctypes binding of libhcr.so, the BF16 hyper-connection read and its Q8_0 sibling (C ABI in include/hcr.h).
 
 Argument marshalling only: tensors are passed as raw device pointers and
 torch's current HIP stream; every step of the read runs in the library's
@@ -41,6 +41,10 @@ def lib():
         L.hcr_geometry.argtypes = [ctypes.POINTER(ip)] * 4
         L.hcr_create.restype = ip
         L.hcr_create.argtypes = [vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
+        L.hcr_create_q8_0.restype = ip
+        L.hcr_create_q8_0.argtypes = [vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
+        L.hcr_quantize_q8_0.restype = ip
+        L.hcr_quantize_q8_0.argtypes = [vp, ip, ip, vp, vp, vp]
         L.hcr_read.restype = ip
         L.hcr_read.argtypes = [vp, ip, vp, vp, vp, vp, vp, vp]
         L.hcr_destroy.restype = None
@@ -92,6 +96,38 @@ def hcr_create(w_down, w_up, w_norm, scratch, scratch_bytes):
     return h.value
 
 
+def hcr_create_q8_0(down_codes, down_scales, up_codes, up_scales, w_norm, scratch, scratch_bytes):
+    """Raw-pointer form (ints or None); returns the handle as an int."""
+    h = ctypes.c_void_p()
+    rc = lib().hcr_create_q8_0(_raw(down_codes), _raw(down_scales), _raw(up_codes), _raw(up_scales), _raw(w_norm),
+                               _raw(scratch), scratch_bytes, ctypes.byref(h))
+    if rc != HCR_OK:
+        raise HCRError(rc, "hcr_create_q8_0")
+    return h.value
+
+
+def hcr_quantize_q8_0(w, rows, cols, codes, scales, stream):
+    """Raw-pointer form (ints or None); returns the status code without raising."""
+    return lib().hcr_quantize_q8_0(_raw(w), int(rows), int(cols), _raw(codes), _raw(scales), _raw(stream))
+
+
+def quantize_q8_0(w, stream=None):
+    """Q8_0 copy of a contiguous BF16 device matrix [rows][cols]: (codes int8 [rows][cols],
+    scales int16 [rows][cols/32] holding binary16 bit patterns), made on the device."""
+    if w.dim() != 2 or not w.is_contiguous() or not w.is_cuda or w.element_size() != 2:
+        raise ValueError("w: a contiguous 2-D BF16 (2-byte) device tensor")
+    rows, cols = w.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.int16, device=w.device)
+    st = current_stream_ptr(w.device) if stream is None else stream
+    rc = hcr_quantize_q8_0(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), st)
+    if rc != HCR_OK:
+        raise HCRError(rc, "hcr_quantize_q8_0")
+    return codes, scales
+
+
 def hcr_read(h, T, x, pending, inj, out, mean, stream):
     """Raw-pointer form (ints or None); returns the status code without raising."""
     return lib().hcr_read(_raw(h), int(T), _raw(x), _raw(pending), _raw(inj), _raw(out), _raw(mean), _raw(stream))
@@ -113,19 +149,38 @@ class HCRead:
     """
 
     def __init__(self, w_down, w_up, w_norm):
+        self._init_common(w_down, w_up, w_norm)
+        self.handle = hcr_create(w_down.data_ptr(), w_up.data_ptr(), w_norm.data_ptr(),
+                                 self.scratch.data_ptr(), self.scratch.numel())
+
+    def _init_common(self, w_down, w_up, w_norm, q8=False):
         S, d, R, self.t_max = hcr_geometry()
         for name, t, shape in (("w_down", w_down, (R, S * d)), ("w_up", w_up, (S * d, R)),
                                ("w_norm", w_norm, (S, d))):
             if tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"{name}: expected a contiguous device tensor of shape {shape}")
-        if w_down.element_size() != 2 or w_up.element_size() != 2 or w_norm.dtype != torch.float32:
-            raise ValueError("weights: BF16 (2-byte) projections and a float32 w_norm")
+        esize = 1 if q8 else 2
+        if w_down.element_size() != esize or w_up.element_size() != esize or w_norm.dtype != torch.float32:
+            raise ValueError("weights: BF16 (2-byte) projections or int8 Q8_0 codes, and a float32 w_norm")
         self.geometry = (S, d, R)
         self.device = w_down.device
         self.w_down, self.w_up, self.w_norm = w_down, w_up, w_norm
         self.scratch = torch.empty(hcr_scratch_bytes(), dtype=torch.uint8, device=self.device)
-        self.handle = hcr_create(w_down.data_ptr(), w_up.data_ptr(), w_norm.data_ptr(),
-                                 self.scratch.data_ptr(), self.scratch.numel())
+
+    @classmethod
+    def q8_0(cls, down_codes, down_scales, up_codes, up_scales, w_norm):
+        """A reader of Q8_0 copies (as ``quantize_q8_0`` makes them) instead of BF16 weights."""
+        self = cls.__new__(cls)
+        self._init_common(down_codes, up_codes, w_norm, q8=True)
+        S, d, R = self.geometry
+        for name, t, shape in (("down_scales", down_scales, (R, S * d // 32)), ("up_scales", up_scales, (S * d, R // 32))):
+            if tuple(t.shape) != shape or not t.is_contiguous() or t.element_size() != 2 or t.device != self.device:
+                raise ValueError(f"{name}: expected contiguous 2-byte {shape} on {self.device}")
+        self.scales = (down_scales, up_scales)
+        self.handle = hcr_create_q8_0(down_codes.data_ptr(), down_scales.data_ptr(), up_codes.data_ptr(),
+                                      up_scales.data_ptr(), w_norm.data_ptr(), self.scratch.data_ptr(),
+                                      self.scratch.numel())
+        return self
 
     def __del__(self):
         h = getattr(self, "handle", None)

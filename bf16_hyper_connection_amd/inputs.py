@@ -137,18 +137,19 @@ def with_near_duplicate_rows(w_down_bits, base, index=0, frac_rows=0.01,
 
 Q8_BLOCK = 32  # weights per block of the Q8_0 copies (along a row)
 Q8_EDGE_FAMILIES = ("normal", "zero", "one_nonzero", "half_integers_amax_127", "tiny", "large", "huge",
-                    "negative_amax", "opposite_amax", "multiples_of_2^-7")
+                    "negative_amax", "opposite_amax", "multiples_of_2^-7", "subnormal_scale")
 
 
 def q8_edge_weights(base, rows=64, K=1024, index=0):
     """BF16 bits [rows][K] whose 32-weight blocks cycle through ``Q8_EDGE_FAMILIES``.
 
-    Block b (row-major over the rows' blocks) has family b mod 10: N(0, 0.02);
+    Block b (row-major over the rows' blocks) has family b mod 11: N(0, 0.02);
     all zero; one nonzero entry; half-integers +-0.5 .. +-126.5 with one +-127
     (a block maximum of 127 puts every entry on a rounding tie); N(0, 1e-7);
     N(0, 1e4); N(0, 1e7); N(0, 0.02) with its largest magnitude made negative;
     two entries +A and -A as the largest magnitudes; integers -127..127 times
-    2**-7 with one +-127.  Every value is drawn in float32 and stored as BF16.
+    2**-7 with one +-127; N(0, 1e-4) (a block maximum whose scale is a binary16
+    subnormal).  Every value is drawn in float32 and stored as BF16.
     """
     if K % Q8_BLOCK:
         raise ValueError("K must be a multiple of 32")
@@ -187,6 +188,8 @@ def q8_edge_weights(base, rows=64, K=1024, index=0):
             v = g.integers(-127, 128, size=Q8_BLOCK).astype(np.float32)
             v[int(g.integers(0, Q8_BLOCK))] = np.float32(127.0 if g.integers(0, 2) else -127.0)
             w[b] = v * np.float32(2.0 ** -7)
+        elif fam == 10:
+            w[b] = np.float32(1e-4) * z
     return f32_to_bf16_bits(w.reshape(rows, K))
 
 

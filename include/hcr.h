@@ -79,6 +79,37 @@ int hcr_geometry(int* streams, int* stream_d, int* rank, int* t_max);
 int hcr_create(const void* w_down, const void* w_up, const float* w_norm,
                void* scratch, size_t scratch_bytes, hcr_t* out);
 
+/* Q8_0 copies (Strata PR #2812, Summary: the sibling read of PR #2810 runs the
+ * same two kernels on Q8_0 copies of the two projections, kept in VRAM beside
+ * the BF16 weights).  The pages do not define the block; this library reads it
+ * as GGML's Q8_0: 32 consecutive weights of a row form a block with one IEEE
+ * binary16 scale d and 32 int8 codes q, a weight being d * q.  Quantisation,
+ * in IEEE binary32: amax = max |w| over the block, d = amax / 127,
+ * q = round(w * (1 / d)) with ties away from zero (q = 0 when d = 0), and the
+ * stored scale is d rounded to binary16 (nearest, ties to even).
+ * Storage is split so that every load stays aligned:
+ *   codes  : int8   [rows][cols]        row-major
+ *   scales : uint16 [rows][cols / 32]   binary16 bit patterns, row-major
+ *
+ * hcr_quantize_q8_0: make the Q8_0 copy of a row-major BF16 matrix w
+ * [rows][cols] (cols a multiple of 32; weights finite) on the device,
+ * asynchronously on `stream` (one kernel; no allocation).  The codes and the
+ * scales are bitwise those of the rule above.  For the read, W_down is
+ * [320][10240] and W_up is [10240][320].  Pointers are device pointers the
+ * caller owns, 16-byte aligned, and codes, scales and w must not overlap.
+ * Errors: HCR_EINVAL (NULL, rows or cols <= 0, cols % 32 != 0, too large),
+ * HCR_EALIGN, HCR_EALIAS (all before any HIP call), HCR_EHIP. */
+int hcr_quantize_q8_0(const void* w, int rows, int cols, void* codes, void* scales, void* stream);
+
+/* Create a handle that reads the Q8_0 copies of one weight set: W_down codes
+ * [320][10240] and scales [320][320], W_up codes [10240][320] and scales
+ * [10240][10], w_norm float [4][2560].  Host-only, as hcr_create; hcr_read
+ * then runs the same read on the decoded weights d * q.  Every pointer must
+ * be 16-byte aligned (scratch 256).  Errors as hcr_create. */
+int hcr_create_q8_0(const void* down_codes, const void* down_scales, const void* up_codes,
+                    const void* up_scales, const float* w_norm, void* scratch, size_t scratch_bytes,
+                    hcr_t* out);
+
 /* One HC read of T tokens, asynchronous on `stream` (a hipStream_t; NULL is the
  * null stream).  Enqueues two kernels and returns; no host synchronisation,
  * allocation or memset, so it can be captured into a HIP graph.
@@ -90,6 +121,7 @@ int hcr_create(const void* w_down, const void* w_up, const float* w_norm,
  *   mean     [T][2560]     written; must not overlap any other buffer
  * T = 0 is an empty read: nothing is enqueued.  Reads on one handle share its
  * scratch and must be ordered on one stream; distinct handles are independent.
+ * The handle's weights may be BF16 (hcr_create) or Q8_0 copies (hcr_create_q8_0).
  * Errors: HCR_EINVAL, HCR_EALIGN, HCR_EALIAS (all before any HIP call), HCR_EHIP. */
 int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj,
              float* out, float* mean, void* stream);

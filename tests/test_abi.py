@@ -26,7 +26,7 @@ def test_geometry_and_scratch(lib):
     n = hcr.hcr_scratch_bytes()
     lo, rs = hcr.hcr_scratch_layout()
     assert n % 256 == 0 and lo % 256 == 0 and rs % 256 == 0
-    assert lo + 8 * 320 * 4 <= rs and rs + 8 * 4 * 4 <= n
+    assert lo + 16 * 320 * 4 <= rs and rs + 16 * 4 * 4 <= n
 
 
 def test_strerror(lib):
@@ -113,3 +113,56 @@ def test_read_null_handle_and_empty(lib):
 
 def test_destroy_null_is_noop(lib):
     hcr.hcr_destroy(None)
+
+
+# ---- Q8_0 entry points (rejections only: a valid call would launch a kernel)
+QD, QDS, QU, QUS = 0xA0000000, 0xB0000000, 0xC0000000, 0xD0000000
+
+
+def _create_q8(**kw):
+    a = dict(dc=QD, ds=QDS, uc=QU, us=QUS, w_norm=WN, scratch=SC, scratch_bytes=hcr.hcr_scratch_bytes())
+    a.update(kw)
+    return hcr.hcr_create_q8_0(a["dc"], a["ds"], a["uc"], a["us"], a["w_norm"], a["scratch"], a["scratch_bytes"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(dc=None), hcr.HCR_EINVAL),
+    (dict(ds=None), hcr.HCR_EINVAL),
+    (dict(us=None), hcr.HCR_EINVAL),
+    (dict(ds=QDS + 2), hcr.HCR_EALIGN),
+    (dict(uc=QU + 8), hcr.HCR_EALIGN),
+    (dict(scratch_bytes=256), hcr.HCR_ESCRATCH),
+    (dict(scratch=QUS + 4096), hcr.HCR_EALIAS),   # inside the up scales (10240 x 10 x 2 bytes)
+    (dict(scratch=QD + MB), hcr.HCR_EALIAS),      # inside the down codes
+])
+def test_create_q8_0_rejects(lib, kw, rc):
+    with pytest.raises(hcr.HCRError) as e:
+        _create_q8(**kw)
+    assert e.value.rc == rc
+
+
+def test_q8_0_read_rejects_out_on_scales(lib):
+    h = _create_q8()
+    try:
+        assert hcr.hcr_read(h, 1, X, None, None, QDS, M, None) == hcr.HCR_EALIAS
+        assert hcr.hcr_read(h, 1, X, None, None, O, QUS + 64, None) == hcr.HCR_EALIAS
+        assert hcr.hcr_read(h, 17, X, None, None, O, M, None) == hcr.HCR_EINVAL
+    finally:
+        hcr.hcr_destroy(h)
+
+
+@pytest.mark.parametrize("args,rc", [
+    (dict(w=None), hcr.HCR_EINVAL),
+    (dict(rows=0), hcr.HCR_EINVAL),
+    (dict(cols=48), hcr.HCR_EINVAL),          # not a multiple of 32
+    (dict(cols=-32), hcr.HCR_EINVAL),
+    (dict(codes=None), hcr.HCR_EINVAL),
+    (dict(w=WD + 8), hcr.HCR_EALIGN),
+    (dict(scales=QDS + 2), hcr.HCR_EALIGN),
+    (dict(codes=WD + 4096), hcr.HCR_EALIAS),  # codes inside w
+    (dict(scales=QD + 1024), hcr.HCR_EALIAS), # scales inside codes
+])
+def test_quantize_q8_0_rejects_before_any_hip_call(lib, args, rc):
+    a = dict(w=WD, rows=320, cols=10240, codes=QD, scales=QDS)
+    a.update(args)
+    assert hcr.hcr_quantize_q8_0(a["w"], a["rows"], a["cols"], a["codes"], a["scales"], None) == rc

@@ -65,6 +65,7 @@ def test_q8_edge_weights_are_seeded_and_cover_every_family():
     a, b = gen.q8_edge_weights(3), gen.q8_edge_weights(3)
     assert np.array_equal(a, b) and a.dtype == np.uint16 and a.shape == (64, 1024)
     blocks = a.reshape(-1, 32)
-    assert not np.any(blocks[1::10])                               # the all-zero family
-    assert np.all(np.count_nonzero(blocks[2::10], axis=1) == 1)   # one nonzero entry
+    n = len(gen.Q8_EDGE_FAMILIES)
+    assert not np.any(blocks[1::n])                               # the all-zero family
+    assert np.all(np.count_nonzero(blocks[2::n], axis=1) == 1)   # one nonzero entry
     assert not np.array_equal(a, gen.q8_edge_weights(4))
