@@ -13,7 +13,6 @@ the read, and the FP64 CPU reference timed on the host as a baseline.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,28 +41,25 @@ def algorithmic_bytes(T, pending=False, inj=False):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hc_read_cold_sweep_traffic.json")
-KERNEL_SOURCES = ["hcr_kernels.hip", "hcr_layout.h", "hcr_api.cpp"]
 
 
-def kernel_source_hash():
-    """sha256 over the HIP sources of the read; counter-derived figures are valid only for this hash."""
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bf16_hyper_connection_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+def algorithmic_bytes_q8(T):
+    """Q8_0 codes and scales of both projections once + w_norm + x read + out and mean written."""
+    return 2 * (R * S * D + R * S * D // 32 * 2) + S * D * 4 + T * (S * D * 4 + S * D * 4 + D * 4)
 
 
-def measured_traffic():
-    """HBM bytes per read from the committed counter summary, or None if the kernels changed since."""
+def measured_traffic(fmt="bf16"):
+    """HBM bytes per read (mean over T = 1..8) from the committed counter summary, or None if the
+    library's sources changed since the counters were taken."""
+    from bf16_hyper_connection_amd import build
     try:
         with open(TRAFFIC_FILE) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256") != kernel_source_hash():
+    if d.get("source_sha256") != build.source_hash():
         return None
-    return d.get("bytes_per_read_mean_T1_8")
+    return d.get(fmt, {}).get("bytes_per_read_mean_T1_8")
 
 
 def log(*a):
@@ -101,6 +97,8 @@ def main():
     ap.add_argument("--sets", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-window", action="store_true", help="skip the 96-read verify window measurement")
+    ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0 copies' per-T measurement")
+    ap.add_argument("--per-t-reps", type=int, default=10, help="graph replays per T for the per-T figures")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -143,16 +141,25 @@ def main():
         torch.cuda.current_stream().wait_stream(stream)
         return g
 
-    def timed(g, reps, warm):
+    marker = torch.zeros(1, device=dev)
+
+    def timed(g, reps, warm, mark=False):
+        """ms for reps replays of g on the bench stream (events on that stream).  With mark, a tiny
+        torch kernel (neg_) runs just before and just after the timed region, outside the events,
+        so that a kernel trace can find the region."""
         with torch.cuda.stream(stream):
             for _ in range(warm):
                 g.replay()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if mark:
+                marker.neg_()
             e0.record(stream)
             for _ in range(reps):
                 g.replay()
             e1.record(stream)
+            if mark:
+                marker.neg_()
             torch.cuda.synchronize()
         return e0.elapsed_time(e1)  # ms
 
@@ -160,8 +167,8 @@ def main():
     per_T_us, per_T_gbps = {}, {}
     for T in range(1, T_WIDE + 1):
         g = capture([T], len(readers))
-        ms = timed(g, 10, 2)
-        us = ms * 1000.0 / (10 * len(readers))
+        ms = timed(g, args.per_t_reps, 2)
+        us = ms * 1000.0 / (args.per_t_reps * len(readers))
         per_T_us[T] = round(us, 3)
         per_T_gbps[T] = round(algorithmic_bytes(T) / us / 1e3, 1)
         log(f"bench: T={T} {us:.3f} us/read  {per_T_gbps[T]:.0f} GB/s")
@@ -173,7 +180,7 @@ def main():
     timed(g, args.warmup, 0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = timed(g, args.steps, 0)
+    ms = timed(g, args.steps, 0, mark=True)
     wall = time.perf_counter() - t0
     ms_per_step = ms / args.steps
     us_per_read = ms_per_step * 1000.0 / reads_per_step
@@ -187,12 +194,65 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("bench: calibration copy of 64 MiB done (4 launches)")
-    traffic = measured_traffic()
+    traffic = measured_traffic("bf16")
+    del g
+
+    q8 = None
+    if not args.no_q8:
+        # Q8_0 copies of the 32 sets, made on the device, and 32 more copies of them in other memory:
+        # 64 rotated sets (445 MB, more than the 256 MB MALL)
+        log("bench: making the Q8_0 copies")
+        qsets = []
+        for r in readers:
+            dc, ds = hcr.quantize_q8_0(r.w_down)
+            uc, us = hcr.quantize_q8_0(r.w_up)
+            qsets.append((dc, ds, uc, us, r.w_norm))
+        qsets += [tuple(t.clone() for t in q) for q in qsets]
+        q8_readers = [hcr.HCRead.q8_0(*q) for q in qsets]
+        # the quantiser itself: both projections of each of the 32 sets (cold), as one graph
+        gq = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gq, stream=stream):
+                for r, q in zip(readers, qsets):
+                    for w, c, sc in ((r.w_down, q[0], q[1]), (r.w_up, q[2], q[3])):
+                        rc = hcr.hcr_quantize_q8_0(w.data_ptr(), w.shape[0], w.shape[1], c.data_ptr(),
+                                                   sc.data_ptr(), stream.cuda_stream)
+                        assert rc == hcr.HCR_OK
+        torch.cuda.current_stream().wait_stream(stream)
+        q_us = timed(gq, 5, 1) * 1000.0 / (5 * 2 * len(readers))
+        del gq
+        q_bytes = R * S * D * (2 + 1) + R * S * D // 32 * 2  # BF16 read, codes and scales written
+        q8_T_us, q8_T_gbps = {}, {}
+        for T in range(1, TMAX + 1):
+            gq = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(gq, stream=stream):
+                    for qr in q8_readers:
+                        qr.read(xs[T], out=outs[T], mean=means[T])
+            torch.cuda.current_stream().wait_stream(stream)
+            us = timed(gq, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(q8_readers))
+            q8_T_us[T] = round(us, 3)
+            q8_T_gbps[T] = round(algorithmic_bytes_q8(T) / us / 1e3, 1)
+            log(f"bench: Q8_0 T={T} {us:.3f} us/read  {q8_T_gbps[T]:.0f} GB/s")
+            del gq
+        mean_us = sum(q8_T_us.values()) / TMAX
+        mean_bytes = sum(algorithmic_bytes_q8(T) for T in range(1, TMAX + 1)) / TMAX
+        q8 = {"per_T_us": q8_T_us, "per_T_algorithmic_GBps": q8_T_gbps, "mean_us_T1_8": round(mean_us, 3),
+              "weight_sets": len(q8_readers), "weight_bytes_per_read": algorithmic_bytes_q8(0) - S * D * 4,
+              "roofline": {"bound": "hbm", "achieved": round(mean_bytes / mean_us / 1e3, 1), "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": round(mean_bytes / mean_us / 1e3 / HBM_PEAK_GBPS, 4),
+                           "traffic": measured_traffic("q8_0")},
+              "quantize_us_per_matrix": round(q_us, 3),
+              "quantize_GBps": round(q_bytes / q_us / 1e3, 1),
+              "note": "Q8_0 copies (GGML block rule) made on the device; 64 rotated sets; per-T graphs of 64 "
+                      "reads replayed 10 times; not part of the timed step"}
+        del q8_readers, qsets
 
     window = None
     if not args.no_window:
         # the verify window: 96 chained reads (out_i = x_{i+1}), distinct weight sets, T = 6, pending on
-        del g
         n_win, t_win = 96, 6
         log(f"bench: generating the {n_win}-read verify window")
         cw = gen.verify_window(n_win, t_win)
@@ -239,7 +299,7 @@ def main():
                                           "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items()
                                                                      if T > TMAX},
                                           "note": "same cold rotation, not part of the timed step"},
-                   "verify_window": window},
+                   "verify_window": window, "q8_0": q8},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "the read (hc_down + hc_up dispatches), event-timed per read over the timed region; "

@@ -1,5 +1,6 @@
 """Build libhcr.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc."""
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -17,6 +18,19 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+
+
+def source_hash():
+    """sha256 over the library's sources (csrc/ and include/hcr.h); measurements taken with
+    hardware counters are valid only for the sources they were taken on."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "hcr.h"), "rb") as fh:
+        h.update(b"hcr.h\0" + fh.read())
+    return h.hexdigest()
 
 
 def hipcc():

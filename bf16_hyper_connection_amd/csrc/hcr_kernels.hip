@@ -510,42 +510,54 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
 }
 
 // ---------------------------------------------------------------------------
-// Q8_0 copies on the device: 4 lanes per 32-weight block (8 BF16 weights each)
+// Q8_0 copies on the device: 4 lanes per 32-weight block (8 BF16 weights each);
+// each lane takes Q8_CHUNKS chunks a grid-stride apart, all loads issued first
 // ---------------------------------------------------------------------------
+constexpr int Q8_CHUNKS = 4;
+
 __global__ __launch_bounds__(256) void q8_quantize(const uint4* __restrict__ w, size_t n_blocks,
                                                    uint2* __restrict__ codes, uint16_t* __restrict__ scales) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // chunk i = block i/4, weights 8(i%4) ..
-  const bool ok = (i >> 2) < n_blocks;                       // a quad is entirely in or out
-  const uint4 u = ok ? w[i] : make_uint4(0, 0, 0, 0);
-  const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-  float f[8];
+  const size_t stride = (size_t)gridDim.x * 256;  // a multiple of 4: a quad stays one block
+  const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 u[Q8_CHUNKS];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __uint_as_float(uu[e] << 16);
-    f[2 * e + 1] = __uint_as_float(uu[e] & 0xffff0000u);
+  for (int k = 0; k < Q8_CHUNKS; ++k) {
+    const size_t i = i0 + k * stride;  // chunk i = block i/4, weights 8(i%4) ..
+    u[k] = (i >> 2) < n_blocks ? w[i] : make_uint4(0, 0, 0, 0);
   }
-  float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
-  amax = fmaxf(amax, dpp<0xB1>(amax));  // quad_perm [1,0,3,2]
-  amax = fmaxf(amax, dpp<0x4E>(amax));  // quad_perm [2,3,0,1]
-  const float d = amax / 127.0f;        // IEEE binary32 division (correctly rounded)
-  const float id = d != 0.f ? 1.0f / d : 0.f;
-  uint32_t packed[2] = {0u, 0u};
+  for (int k = 0; k < Q8_CHUNKS; ++k) {
+    const size_t i = i0 + k * stride;
+    const uint32_t uu[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+    float f[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int qv = static_cast<int>(__builtin_roundf(f[e] * id));  // ties away from zero
-    packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * (e & 3));
-  }
-  if (ok) {
-    codes[i] = make_uint2(packed[0], packed[1]);
-    if ((i & 3) == 0) scales[i >> 2] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d));
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(uu[e] << 16);
+      f[2 * e + 1] = __uint_as_float(uu[e] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+    amax = fmaxf(amax, dpp<0xB1>(amax));  // quad_perm [1,0,3,2]
+    amax = fmaxf(amax, dpp<0x4E>(amax));  // quad_perm [2,3,0,1]
+    const float d = amax / 127.0f;        // IEEE binary32 division (correctly rounded)
+    const float id = d != 0.f ? 1.0f / d : 0.f;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qv = static_cast<int>(__builtin_roundf(f[e] * id));  // ties away from zero
+      packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xffu) << (8 * (e & 3));
+    }
+    if ((i >> 2) < n_blocks) {  // a quad is entirely in or out
+      codes[i] = make_uint2(packed[0], packed[1]);
+      if ((i & 3) == 0) scales[i >> 2] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d));
+    }
   }
 }
 
 int launch_quantize_q8_0(const void* w, size_t n_blocks, void* codes, void* scales, void* stream) {
-  const size_t threads = n_blocks * 4;
-  const size_t wgs = (threads + 255) / 256;
+  const size_t chunks = n_blocks * 4;
+  const size_t wgs = (chunks + 256 * Q8_CHUNKS - 1) / (256 * Q8_CHUNKS);
   (void)hipGetLastError();
   hipLaunchKernelGGL(q8_quantize, dim3(static_cast<unsigned>(wgs)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const uint4*>(w), n_blocks,

@@ -1,0 +1,203 @@
+"""Summarise rocprofv3 output of ``bench.py`` into the kernel-duration and HBM-traffic records.
+
+Inputs are the CSV files of three runs of the same bench command:
+
+* ``--trace``: ``rocprofv3 --kernel-trace --stats --output-format csv`` (``*_kernel_stats.csv``);
+* ``--fetch`` / ``--write``: ``rocprofv3 --pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` with
+  ``--kernel-trace`` (``*_counter_collection.csv``), run with ``bench.py --calibrate-copy`` so
+  that a 64 MiB device copy (the runtime's copyBuffer kernel) gives the counters' scale.
+
+Writes a markdown table (average duration and HBM bytes per read, per T and weight format) and
+the JSON traffic record that ``bench.py`` reads, keyed to the library's source hash.
+
+    python -m bf16_hyper_connection_amd.rocprof_summary --trace DIR --fetch DIR --write DIR \\
+        --md profiles/x.md --json profiles/x.json --command "..." --command "..."
+"""
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import re
+import statistics
+
+from bf16_hyper_connection_amd import build
+
+S, D, R = 4, 2560, 320
+FORMATS = {0: "bf16", 1: "q8_0"}
+COPY_BYTES = 64 << 20
+
+
+def algorithmic_bytes(fmt, T):
+    w = 2 * R * S * D * 2 if fmt == 0 else 2 * (R * S * D + R * S * D // 32 * 2)
+    return w + S * D * 4 + T * (S * D * 4 + S * D * 4 + D * 4)
+
+
+def kernel_key(name):
+    """('down'|'up', T, fmt, inj, pend) of a read kernel's demangled name, ('quantize',) or None."""
+    m = re.search(r"hcr::hc_down<(\d+), (\d+)>", name)
+    if m:
+        return ("down", int(m.group(1)), int(m.group(2)), False, False)
+    m = re.search(r"hcr::hc_up<(\d+), (true|false), (true|false), (\d+)>", name)
+    if m:
+        return ("up", int(m.group(1)), int(m.group(4)), m.group(2) == "true", m.group(3) == "true")
+    if "hcr::q8_quantize" in name:
+        return ("quantize",)
+    return None
+
+
+def _one(pattern, d):
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one {pattern} under {d}, found {files}")
+    return files[0]
+
+
+def durations(trace_dir):
+    out = {}
+    with open(_one("*kernel_stats.csv", trace_dir)) as fh:
+        for r in csv.DictReader(fh):
+            k = kernel_key(r["Name"])
+            if k:
+                out[k] = (float(r["AverageNs"]) / 1000.0, int(r["Calls"]))
+    return out
+
+
+def timed_region(trace_dir):
+    """The read dispatches between the last two marker kernels (bench.py runs a torch neg_ kernel just
+    before and just after its timed region): (reads, mean µs per read from first start to last end,
+    mean down µs, mean up µs)."""
+    with open(_one("*kernel_trace.csv", trace_dir)) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+    marks = [i for i, r in enumerate(rows) if "neg_kernel" in r["Kernel_Name"]]
+    if len(marks) < 2:
+        return None
+    region = [r for r in rows[marks[-2] + 1:marks[-1]] if kernel_key(r["Kernel_Name"])]
+    if not region:
+        return None
+    dur = collections.defaultdict(list)
+    for r in region:
+        dur[kernel_key(r["Kernel_Name"])[0]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    reads = len(dur["down"])
+    span = (max(int(r["End_Timestamp"]) for r in region) - min(int(r["Start_Timestamp"]) for r in region)) / 1000.0
+    return reads, span / reads, statistics.mean(dur["down"]), statistics.mean(dur["up"])
+
+
+def counters(d, counter):
+    vals, copy = collections.defaultdict(list), []
+    with open(_one("*counter_collection.csv", d)) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            k = kernel_key(r["Kernel_Name"])
+            if k:
+                vals[k].append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and v > 8192:
+                copy.append(v)
+    if not copy:
+        raise SystemExit(f"no calibration copy in {d}: run bench.py with --calibrate-copy")
+    return {k: statistics.median(v) for k, v in vals.items()}, statistics.median(copy)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--md", required=True)
+    ap.add_argument("--json", required=True)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--bench-log", help="stdout of the traced bench run (its JSON line: the traced event figure)")
+    ap.add_argument("--bench-json", help="the JSON line of an untraced bench.py run of the same session")
+    a = ap.parse_args()
+
+    dur = durations(a.trace)
+    fetch, fetch_copy = counters(a.fetch, "FETCH_SIZE")
+    write, write_copy = counters(a.write, "WRITE_SIZE")
+    fs, ws = COPY_BYTES / 1024.0 / fetch_copy, COPY_BYTES / 1024.0 / write_copy
+
+    rec = {"about": "HBM bytes per read (down + up kernels, no pending write or injection) on MI355X from two "
+                    "rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled by the same counter for a "
+                    f"64 MiB device copy: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}",
+           "commands": a.command, "fetch_scale": fs, "write_scale": ws,
+           "calibration_copy_KiB": {"bytes": COPY_BYTES, "FETCH_SIZE": fetch_copy, "WRITE_SIZE": write_copy},
+           "source_sha256": build.source_hash()}
+    lines = ["| format | T | down avg µs | up avg µs | sum µs | down FETCH KiB | up FETCH KiB | down WRITE KiB | "
+             "up WRITE KiB | HBM bytes/read (scaled) | algorithmic bytes/read |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for fmt, fname in FORMATS.items():
+        per_T, tot = {}, []
+        for T in range(1, 17):
+            kd, ku = ("down", T, fmt, False, False), ("up", T, fmt, False, False)
+            if kd not in dur or ku not in dur:
+                continue
+            f_d, f_u = fetch.get(kd), fetch.get(ku)
+            w_d, w_u = write.get(kd), write.get(ku)
+            row = {"down_us": round(dur[kd][0], 3), "up_us": round(dur[ku][0], 3),
+                   "calls": dur[kd][1], "algorithmic_bytes": algorithmic_bytes(fmt, T)}
+            if None not in (f_d, f_u, w_d, w_u):
+                fb, wb = (f_d + f_u) * 1024 * fs, (w_d + w_u) * 1024 * ws
+                row.update(fetch_bytes=int(round(fb)), write_bytes=int(round(wb)), total_bytes=int(round(fb + wb)))
+                if T <= 8:
+                    tot.append(fb + wb)
+            per_T[str(T)] = row
+            lines.append(f"| {fname} | {T} | {row['down_us']:.3f} | {row['up_us']:.3f} | "
+                         f"{row['down_us'] + row['up_us']:.3f} | "
+                         + " | ".join("—" if v is None else f"{v:.1f}" for v in (f_d, f_u, w_d, w_u))
+                         + " | " + (f"{row['total_bytes']:,}" if "total_bytes" in row else "—")
+                         + f" | {row['algorithmic_bytes']:,} |")
+        if per_T:
+            rec[fname] = {"per_T": per_T,
+                          "bytes_per_read_mean_T1_8": int(round(sum(tot) / len(tot))) if len(tot) == 8 else None}
+    tr = timed_region(a.trace)
+    if tr:
+        rec["timed_region"] = {"reads": tr[0], "us_per_read": round(tr[1], 3), "down_avg_us": round(tr[2], 3),
+                               "up_avg_us": round(tr[3], 3)}
+    q = ("quantize",)
+    if q in dur:
+        rec["q8_0_quantize"] = {"avg_us": round(dur[q][0], 3), "calls": dur[q][1],
+                                "fetch_KiB": fetch.get(q), "write_KiB": write.get(q)}
+
+    with open(a.json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    md = ["# Kernel durations and HBM traffic per read (MI355X)", "",
+          "Commands (from the repository root on the GPU box):", "", "```"] + a.command + ["```", "",
+          f"Counter scale from a 64 MiB device copy in the same runs: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}.",
+          f"Library sources sha256 {rec['source_sha256'][:16]}…", ""] + lines
+    for fname in FORMATS.values():
+        if fname in rec and rec[fname]["bytes_per_read_mean_T1_8"]:
+            alg = sum(algorithmic_bytes(0 if fname == "bf16" else 1, T) for T in range(1, 9)) / 8
+            b = rec[fname]["bytes_per_read_mean_T1_8"]
+            md.append("")
+            md.append(f"{fname}: mean over T = 1..8, {b:,} HBM bytes per read vs {int(alg):,} algorithmic "
+                      f"({100.0 * (b / alg - 1):+.1f} %).")
+    if tr:
+        def last_json(path):
+            if not path:
+                return None
+            with open(path) as fh:
+                js = [ln for ln in fh if ln.startswith("{")]
+            return json.loads(js[-1])["value"] if js else None
+        traced, untraced = last_json(a.bench_log), last_json(a.bench_json)
+        rec["timed_region"].update(bench_event_us_per_read_untraced=untraced, bench_event_us_per_read_traced=traced)
+        tot = tr[2] + tr[3]
+        md += ["", f"Timed region of the traced bench run (its timed steps, found between two marker kernels): "
+                   f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + hc_up {tr[3]:.3f} µs = "
+                   f"{tot:.3f} µs per read."
+                   + (f" An untraced `python bench.py` of the same session measured {untraced:.3f} µs per read "
+                      f"event-timed (its `value`; {100 * tot / untraced - 100:+.1f} %)." if untraced else "")
+                   + (f" Under the tracer the dispatches are spaced out: the traced run's own event figure is "
+                      f"{traced:.3f} µs per read." if traced else "")]
+    if q in dur:
+        md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
+                   f"{dur[q][1]} calls."]
+    with open(a.md, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+
+
+if __name__ == "__main__":
+    main()
