@@ -31,7 +31,7 @@ T_MAX = 8       # largest verify window the pages measure
 T_WIDE = 16     # larger windows, also generated
 
 # purposes (second element of a seed key)
-_P_WDOWN, _P_WUP, _P_WNORM, _P_X, _P_PENDING, _P_INJ, _P_NEARDUP, _P_EDGE = range(1, 9)
+_P_WDOWN, _P_WUP, _P_WNORM, _P_X, _P_PENDING, _P_INJ, _P_NEARDUP, _P_EDGE, _P_MV_W, _P_MV_X = range(1, 11)
 
 
 def rng(*key):
@@ -191,6 +191,21 @@ def q8_edge_weights(base, rows=64, K=1024, index=0):
         elif fam == 10:
             w[b] = np.float32(1e-4) * z
     return f32_to_bf16_bits(w.reshape(rows, K))
+
+
+MV_ROWS, MV_COLS, MV_T_MAX = 12288, 2560, 4  # the pages' attn_q projection, 1..4 columns
+
+
+def matvec_weights(base, index=0, rows=MV_ROWS, cols=MV_COLS):
+    """W ~ N(0, 1/sqrt(cols)) as BF16 bits [rows][cols] (one copy of the skinny matvec's weights)."""
+    w = rng(base, _P_MV_W, index).standard_normal((rows, cols), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(cols))
+    return f32_to_bf16_bits(w)
+
+
+def matvec_x(base, T, index=0, cols=MV_COLS):
+    """x ~ N(0, 1), float32 [T][cols]."""
+    return rng(base, _P_MV_X, index).standard_normal((T, cols), dtype=np.float32)
 
 
 # ---------------------------------------------------------------------------

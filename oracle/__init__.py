@@ -1,4 +1,4 @@
-"""FP64 CPU reference ("oracle") of the BF16 hyper-connection read and of its Q8_0 sibling.
+"""FP64 CPU reference ("oracle") of the BF16 hyper-connection read, its Q8_0 sibling and the skinny BF16 matvec.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import, call or run anything in this
@@ -17,3 +17,4 @@ from .reference import (  # noqa: F401
     up_projection,
 )
 from .q8_0 import dequantize_q8_0, hc_read_q8_0, quantize_q8_0  # noqa: F401,E402
+from .matvec import matvec_bf16  # noqa: F401,E402
