@@ -99,6 +99,7 @@ def main():
     ap.add_argument("--no-window", action="store_true", help="skip the 96-read verify window measurement")
     ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0 copies' per-T measurement")
     ap.add_argument("--per-t-reps", type=int, default=10, help="graph replays per T for the per-T figures")
+    ap.add_argument("--no-matvec", action="store_true", help="skip the skinny BF16 matvec measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -250,6 +251,42 @@ def main():
                       "reads replayed 10 times; not part of the timed step"}
         del q8_readers, qsets
 
+    matvec = None
+    if not args.no_matvec:
+        # the skinny BF16 matvec, 12288 x 2560 (63 MB), 8 copies rotated (503 MB, more than the MALL)
+        log("bench: generating the matvec weights")
+        n_mv, rows, cols = 8, gen.MV_ROWS, gen.MV_COLS
+        mw = [torch.from_numpy(gen.matvec_weights(30, k).view(np.int16)).to(dev) for k in range(n_mv)]
+        mv_T_us, mv_T_gbps = {}, {}
+        for T in range(1, gen.MV_T_MAX + 1):
+            mx = torch.from_numpy(gen.matvec_x(30, T)).to(dev)
+            my = torch.empty((T, rows), device=dev)
+            gm = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(gm, stream=stream):
+                    for k in range(n_mv):
+                        rc = hcr.hcr_matvec_bf16(mw[k].data_ptr(), rows, cols, T, mx.data_ptr(), my.data_ptr(),
+                                                 stream.cuda_stream)
+                        assert rc == hcr.HCR_OK
+            torch.cuda.current_stream().wait_stream(stream)
+            reps = max(args.per_t_reps, 1) * 2
+            us = timed(gm, reps, 2) * 1000.0 / (reps * n_mv)
+            b = rows * cols * 2 + T * cols * 4 + T * rows * 4
+            mv_T_us[T] = round(us, 3)
+            mv_T_gbps[T] = round(b / us / 1e3, 1)
+            log(f"bench: matvec T={T} {us:.3f} us/call  {mv_T_gbps[T]:.0f} GB/s")
+            del gm
+        best = max(mv_T_gbps.values())
+        matvec = {"shape": [rows, cols], "copies": n_mv, "per_T_us": mv_T_us, "per_T_algorithmic_GBps": mv_T_gbps,
+                  "roofline": {"bound": "hbm", "achieved": round(sum(mv_T_gbps.values()) / len(mv_T_gbps), 1),
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(sum(mv_T_gbps.values()) / len(mv_T_gbps) / HBM_PEAK_GBPS, 4),
+                               "best_frac": round(best / HBM_PEAK_GBPS, 4)},
+                  "note": "y = W x, BF16 weights, 1..4 columns; graphs of 8 calls over the rotated copies; "
+                          "not part of the timed step"}
+        del mw
+
     window = None
     if not args.no_window:
         # the verify window: 96 chained reads (out_i = x_{i+1}), distinct weight sets, T = 6, pending on
@@ -299,7 +336,7 @@ def main():
                                           "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items()
                                                                      if T > TMAX},
                                           "note": "same cold rotation, not part of the timed step"},
-                   "verify_window": window, "q8_0": q8},
+                   "verify_window": window, "q8_0": q8, "matvec_bf16": matvec},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "the read (hc_down + hc_up dispatches), event-timed per read over the timed region; "

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhcr.so")
 
-SOURCES = ["hcr_kernels.hip", "hcr_api.cpp"]
+SOURCES = ["hcr_kernels.hip", "hcr_matvec.hip", "hcr_api.cpp"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed FP32 instructions in device code (the host pass ignores the feature)

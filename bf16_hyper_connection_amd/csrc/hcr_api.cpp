@@ -111,6 +111,18 @@ int hcr_quantize_q8_0(const void* w, int rows, int cols, void* codes, void* scal
   return hcr::launch_quantize_q8_0(w, n / hcr::Q8_BLOCK, codes, scales, stream);
 }
 
+int hcr_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, float* y, void* stream) {
+  if (T == 0) return HCR_OK;
+  if (!w || !x || !y || rows <= 0 || cols <= 0 || cols % 8 || cols > 64 * 8 * hcr::MV_KCH_MAX || T < 0 ||
+      T > hcr::MV_T_MAX)
+    return HCR_EINVAL;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16)) return HCR_EALIGN;
+  const Span sw = span(w, size_t(rows) * size_t(cols) * 2), sx = span(x, size_t(T) * cols * 4),
+             sy = span(y, size_t(T) * rows * 4);
+  if (overlap(sy, sw) || overlap(sy, sx)) return HCR_EALIAS;
+  return hcr::launch_matvec_bf16(w, rows, cols, T, x, y, stream);
+}
+
 int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj, float* out, float* mean,
              void* stream) {
   if (!h || T < 0 || T > hcr::TMAX) return HCR_EINVAL;

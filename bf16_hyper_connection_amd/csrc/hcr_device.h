@@ -1,0 +1,104 @@
+// Device helpers shared by the HIP kernels of this library (gfx950, wave64):
+// vector types, exact BF16 / binary16 / int8 widening, the BF16 high/low split,
+// DPP lane moves and the fixed-order multi-value wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hcr {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// byte k of u as a signed 8-bit code, widened exactly to FP32
+__device__ __forceinline__ float code(uint32_t u, int k) {
+  return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(u >> (8 * k))));
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Split 8 FP32 values into BF16 high parts (round to nearest even) and the
+// BF16-rounded remainders; returns the packed high (hi) and low (lo) words.
+__device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 a = {v[2 * e], v[2 * e + 1]};
+    const bf16x2 bh = __builtin_convertvector(a, bf16x2);
+    const f32x2 r = a - __builtin_convertvector(bh, f32x2);  // exact
+    const bf16x2 bl = __builtin_convertvector(r, bf16x2);
+    h[e] = __builtin_bit_cast(uint32_t, bh);
+    l[e] = __builtin_bit_cast(uint32_t, bl);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+__device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum N values per lane over the 64 lanes of a wave (N a multiple of 4).  Two
+// halving steps (v_permlane32_swap, v_permlane16_swap) then a butterfly inside
+// each row of 16 lanes; afterwards every lane l holds, in v[0 .. N/4), the
+// totals of values (l >> 4) * N/4 + i.  The order of the additions is fixed.
+template <int N>
+__device__ __forceinline__ void wave_sum(float (&v)[N]) {
+  static_assert(N % 4 == 0, "wave_sum needs a multiple of 4 values");
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // lanes < 32: value i; lanes >= 32: value i + N/2
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 4]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // even rows: value i; odd rows: value i + N/4
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    v[i] += dpp<0xB1>(v[i]);   // quad_perm [1,0,3,2]
+    v[i] += dpp<0x4E>(v[i]);   // quad_perm [2,3,0,1]
+    v[i] += dpp<0x141>(v[i]);  // row_half_mirror
+    v[i] += dpp<0x140>(v[i]);  // row_mirror
+  }
+}
+
+constexpr int round4(int n) { return (n + 3) & ~3; }
+
+// Sum N values per lane over the 32 lanes of each half-wave (N even): one halving
+// step (v_permlane16_swap) then a butterfly inside each row of 16 lanes.  Lanes
+// of row (l >> 4) & 1 then hold, in v[0 .. N/2), the half-wave totals of values
+// ((l >> 4) & 1) * N/2 + i.
+template <int N>
+__device__ __forceinline__ void half_wave_sum(float (&v)[N]) {
+  static_assert(N % 2 == 0, "half_wave_sum needs an even number of values");
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false, false);
+    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    v[i] += dpp<0xB1>(v[i]);
+    v[i] += dpp<0x4E>(v[i]);
+    v[i] += dpp<0x141>(v[i]);
+    v[i] += dpp<0x140>(v[i]);
+  }
+}
+
+constexpr int round2(int n) { return (n + 1) & ~1; }
+
+}  // namespace hcr

@@ -51,6 +51,16 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
                 const float* w_norm, void* scratch, const float* x, const float* pending, const float* inj,
                 float* out, float* mean, void* stream);
 
+// ---- skinny BF16 matvec: a wave takes one group of MV_ROWS_PER_WAVE rows
+constexpr int MV_THREADS = 256;
+constexpr int MV_ROWS_PER_WAVE = 4;
+constexpr int MV_MAX_WGS = 65536;  // beyond it (rows > 1M) the waves walk the matrix in steps
+constexpr int MV_T_MAX = 4;      // columns per call
+constexpr int MV_KCH_MAX = 6;    // 16-byte chunks per lane and row: cols <= 64 * 8 * 6 = 3072 (no register spills at T = 4)
+
+// Enqueue y = W x for T columns (arguments already validated: cols % 8 == 0, cols <= 3072, T in 1..4).
+int launch_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, float* y, void* stream);
+
 // Enqueue the Q8_0 quantisation of n_blocks 32-weight blocks (arguments already validated).
 int launch_quantize_q8_0(const void* w, size_t n_blocks, void* codes, void* scales, void* stream);
 

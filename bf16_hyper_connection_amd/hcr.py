@@ -45,6 +45,8 @@ def lib():
         L.hcr_create_q8_0.argtypes = [vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
         L.hcr_quantize_q8_0.restype = ip
         L.hcr_quantize_q8_0.argtypes = [vp, ip, ip, vp, vp, vp]
+        L.hcr_matvec_bf16.restype = ip
+        L.hcr_matvec_bf16.argtypes = [vp, ip, ip, ip, vp, vp, vp]
         L.hcr_read.restype = ip
         L.hcr_read.argtypes = [vp, ip, vp, vp, vp, vp, vp, vp]
         L.hcr_destroy.restype = None
@@ -126,6 +128,30 @@ def quantize_q8_0(w, stream=None):
     if rc != HCR_OK:
         raise HCRError(rc, "hcr_quantize_q8_0")
     return codes, scales
+
+
+def hcr_matvec_bf16(w, rows, cols, T, x, y, stream):
+    """Raw-pointer form of hcr_matvec_bf16 (ints or None); returns the status code without raising."""
+    return lib().hcr_matvec_bf16(_raw(w), int(rows), int(cols), int(T), _raw(x), _raw(y), _raw(stream))
+
+
+def matvec_bf16(w, x, y=None, stream=None):
+    """y [T][rows] = x [T][cols] times W^T, W a contiguous BF16 (2-byte) device matrix [rows][cols]."""
+    if w.dim() != 2 or not w.is_contiguous() or not w.is_cuda or w.element_size() != 2:
+        raise ValueError("w: a contiguous 2-D BF16 (2-byte) device tensor")
+    rows, cols = w.shape
+    if x.dim() != 2 or x.shape[1] != cols or x.dtype != torch.float32 or not x.is_contiguous() or x.device != w.device:
+        raise ValueError(f"x: contiguous float32 [T][{cols}] on {w.device}")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, rows), dtype=torch.float32, device=w.device)
+    if tuple(y.shape) != (T, rows) or y.dtype != torch.float32 or not y.is_contiguous() or y.device != w.device:
+        raise ValueError(f"y: contiguous float32 [{T}][{rows}] on {w.device}")
+    st = current_stream_ptr(w.device) if stream is None else stream
+    rc = hcr_matvec_bf16(w.data_ptr(), rows, cols, T, x.data_ptr(), y.data_ptr(), st)
+    if rc != HCR_OK:
+        raise HCRError(rc, "hcr_matvec_bf16")
+    return y
 
 
 def hcr_read(h, T, x, pending, inj, out, mean, stream):

@@ -110,6 +110,20 @@ int hcr_create_q8_0(const void* down_codes, const void* down_scales, const void*
                     const void* up_scales, const float* w_norm, void* scratch, size_t scratch_bytes,
                     hcr_t* out);
 
+/* Skinny BF16 matrix-vector product, the second workload of the pages' decode
+ * window (Strata PR #2221, first comment: the attn_q projection, 2,560 inputs to
+ * 12,288 outputs, at one to four columns, cold weights; the pages' Q2_0 format is
+ * not defined there, so the weights here are BF16):
+ *   y[t][n] = sum_k W[n][k] * x[t][k],   t < T, n < rows, k < cols
+ *   w : BF16 [rows][cols] row-major      x : float [T][cols]      y : float [T][rows]
+ * Asynchronous on `stream` (one kernel; no allocation, no memset).  FP32
+ * accumulation in a fixed order (bitwise reproducible).  rows >= 1, cols a
+ * multiple of 8 and at most 3072, T in 0..4 (T = 0 enqueues nothing); w and x
+ * finite.  Device pointers the caller owns, 16-byte aligned; y must not overlap
+ * w or x.
+ * Errors: HCR_EINVAL, HCR_EALIGN, HCR_EALIAS (all before any HIP call), HCR_EHIP. */
+int hcr_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, float* y, void* stream);
+
 /* One HC read of T tokens, asynchronous on `stream` (a hipStream_t; NULL is the
  * null stream).  Enqueues two kernels and returns; no host synchronisation,
  * allocation or memset, so it can be captured into a HIP graph.

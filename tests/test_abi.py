@@ -166,3 +166,28 @@ def test_quantize_q8_0_rejects_before_any_hip_call(lib, args, rc):
     a = dict(w=WD, rows=320, cols=10240, codes=QD, scales=QDS)
     a.update(args)
     assert hcr.hcr_quantize_q8_0(a["w"], a["rows"], a["cols"], a["codes"], a["scales"], None) == rc
+
+
+@pytest.mark.parametrize("args,rc", [
+    (dict(w=None), hcr.HCR_EINVAL),
+    (dict(x=None), hcr.HCR_EINVAL),
+    (dict(y=None), hcr.HCR_EINVAL),
+    (dict(rows=0), hcr.HCR_EINVAL),
+    (dict(cols=2564), hcr.HCR_EINVAL),          # not a multiple of 8
+    (dict(cols=3080), hcr.HCR_EINVAL),          # more than 3072
+    (dict(T=5), hcr.HCR_EINVAL),
+    (dict(T=-1), hcr.HCR_EINVAL),
+    (dict(w=WD + 8), hcr.HCR_EALIGN),
+    (dict(x=X + 4), hcr.HCR_EALIGN),
+    (dict(y=O + 4), hcr.HCR_EALIGN),
+    (dict(y=WD + 4096), hcr.HCR_EALIAS),        # y inside w
+    (dict(y=X + 16), hcr.HCR_EALIAS),           # y overlapping x
+])
+def test_matvec_rejects_before_any_hip_call(lib, args, rc):
+    a = dict(w=WD, rows=12288, cols=2560, T=2, x=X, y=O)
+    a.update(args)
+    assert hcr.hcr_matvec_bf16(a["w"], a["rows"], a["cols"], a["T"], a["x"], a["y"], None) == rc
+
+
+def test_matvec_empty_is_noop(lib):
+    assert hcr.hcr_matvec_bf16(None, 0, 0, 0, None, None, None) == hcr.HCR_OK
