@@ -319,6 +319,24 @@ def main():
                   "note": "one HIP graph of the 96-read residual chain, distinct BF16 weight sets (1.26 GB)"}
         log(f"bench: window {window['us_per_window']} us ({window['us_per_read']} us/read, "
             f"{window['algorithmic_GBps']} GB/s)")
+        # the same chain with its weights resident in the MALL (16 sets, 210 MB, reused in turn): the bound
+        # that prefetching the next read's weights into the MALL could reach
+        del gw
+        gh = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gh, stream=stream):
+                xx = wx0
+                for i in range(n_win):
+                    wreaders[i % 16].read(xx, wpend[i], None, out=wouts[i], mean=wmeans[i])
+                    xx = wouts[i]
+        torch.cuda.current_stream().wait_stream(stream)
+        hms = timed(gh, reps, 3) / reps
+        window["mall_resident_us_per_window"] = round(hms * 1000, 2)
+        window["mall_resident_note"] = ("the same chain over 16 weight sets (210 MB, resident in the 256 MB MALL): "
+                                        "the bound of prefetching the next read's weights into the MALL")
+        log(f"bench: window with MALL-resident weights {window['mall_resident_us_per_window']} us")
+        del gh
 
     line = {
         "metric": METRIC, "value": round(us_per_read, 3), "unit": "µs", "n_gpus": 1,

@@ -7,13 +7,15 @@
 //
 //   hc_down<T>: norm statistics + down projection + split-reduction finish.
 //     A work-group owns one whole stream (2,560 columns) of 5 W_down rows, so
-//     it can apply rs itself: every lane owns 10 columns (one 16-byte chunk
-//     and one dword of each row, both coalesced across the wave), computes
-//     x*w_norm and the sums of squares of its columns for the T tokens, and
-//     one FP32 FMA chain per (row, token) over the exactly widened BF16
-//     weights.  The 6T per-lane values are summed over the wave (halving with
-//     v_permlane32/16_swap, then DPP) and over the 4 waves (LDS, fixed order);
-//     the work-group writes rs[t][s] * (row sums), one partial per stream.
+//     it can apply rs itself: 8 waves (two per SIMD, so that one wave's
+//     arithmetic overlaps the other's waits), every lane owning 5 columns (an
+//     8-byte and a 2-byte piece of each row, both coalesced across the wave);
+//     the lane computes x*w_norm and the sums of squares of its columns for
+//     the T tokens, and one FP32 FMA chain per (row, token) over the exactly
+//     widened BF16 weights.  The 6T per-lane values are summed over the wave
+//     (halving with v_permlane32/16_swap, then DPP) and over the 8 waves (LDS,
+//     fixed order); the work-group writes rs[t][s] * (row sums), one partial
+//     per stream.
 //   hc_up<T, INJ, PEND>: lo[t][k] = the 4 stream partials (+ injection), then
 //     40 rows of W_up (10 columns x 4 streams) per work-group.  Each row is
 //     reduced by the 32 lanes of a half-wave; lane q owns K [8q, 8q+8) and
@@ -51,9 +53,8 @@
 // Q8_0 copies (Strata PR #2812, Summary: the sibling read of #2810 on Q8_0
 // copies of the projections; the block is read as GGML's Q8_0: 32 weights of
 // a row share one binary16 scale d, each weight is d times an int8 code).
-// The same two kernels, templated on the weight format, read int8 codes (8 +
-// 2 per lane and row, half the bytes of BF16) and two scales per lane and
-// row; a lane's 8-column chunk and its 2-column chunk each sit inside one
+// The same two kernels, templated on the weight format, read int8 codes (half
+// the bytes of BF16) and two scales per lane and row; a lane's 8-column chunk and its 2-column chunk each sit inside one
 // block, so the lane multiplies each chunk's FMA sum by its block's scale.
 // The up kernel takes lo in FP32 from LDS (no BF16 split): the codes widen
 // exactly to FP32.  q8_quantize makes the copies on the device: 4 lanes per
@@ -73,6 +74,25 @@
 namespace hcr {
 
 // down: one stream x 5 rows per work-group; rs applied here (the work-group sees the whole stream)
+// x (or w_norm) values of a lane's two column runs: CA columns at ca and CB at cb
+template <int CA, int CB>
+struct Cols {
+  float a[CA], b[CB];
+  __device__ __forceinline__ void load(const float* p, int ca, int cb) {
+#pragma unroll
+    for (int e = 0; e < CA; e += 4) {
+      const f32x4 v = ld4(p + ca + e);
+      a[e] = v[0], a[e + 1] = v[1], a[e + 2] = v[2], a[e + 3] = v[3];
+    }
+    if constexpr (CB == 2) {
+      const f32x2 v = ld2(p + cb);
+      b[0] = v[0], b[1] = v[1];
+    } else {
+      b[0] = p[cb];
+    }
+  }
+};
+
 template <int T, int FMT>
 __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__ w_down,
                                                            const uint16_t* __restrict__ s_down,
@@ -83,50 +103,60 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
   const int s = blockIdx.x & (S - 1);
   const int g = blockIdx.x >> 2;  // rows DOWN_ROWS*g ..
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ca = 512 * wave + 8 * lane;         // 8 columns: one 16-byte chunk per row
-  const int cb = 2048 + 128 * wave + 2 * lane;  // 2 columns: one dword per row
+  constexpr int CA = DOWN_CA, CB = DOWN_CB, NC = CA + CB;
+  const int ca = (2048 / DOWN_WAVES) * wave + CA * lane;        // CA columns: one 2*CA-byte chunk per row
+  const int cb = 2048 + (512 / DOWN_WAVES) * wave + CB * lane;  // CB columns
 
   // Tokens are taken in groups of up to 8 (x of one group in registers at a time).
   constexpr int TG = T < 8 ? T : 8;
   constexpr int NG = (T + TG - 1) / TG;
-  f32x4 xa0[TG], xa1[TG];
-  f32x2 xb[TG];
+  Cols<CA, CB> xv[TG];
   auto load_x = [&](int grp) {
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int t = grp * TG + i;
-      if (t < T) {
-        const float* xt = x + ((size_t)t * S + s) * D;
-        xa0[i] = ld4(xt + ca);
-        xa1[i] = ld4(xt + ca + 4);
-        xb[i] = ld2(xt + cb);
-      }
+      if (t < T) xv[i].load(x + ((size_t)t * S + s) * D, ca, cb);
     }
   };
 
   // 1. x of the first group and w_norm first (vector loads complete in issue order), then the 5 weight rows
   load_x(0);
-  const float* ns = w_norm + s * D;
-  const f32x4 na0 = ld4(ns + ca), na1 = ld4(ns + ca + 4);
-  const f32x2 nb = ld2(ns + cb);
-  uint4 wa[DOWN_ROWS];      // BF16: 8 weights at ca
-  uint32_t wb[DOWN_ROWS];   // BF16: 2 weights at cb; Q8_0: 2 codes at cb
-  uint2 qa[DOWN_ROWS];      // Q8_0: 8 codes at ca
+  Cols<CA, CB> nv;
+  nv.load(w_norm + s * D, ca, cb);
+  uint32_t wa[DOWN_ROWS][CA / 2];  // BF16: CA weights at ca (packed pairs); Q8_0: CA codes (packed quads)
+  uint32_t wb[DOWN_ROWS];          // BF16 / Q8_0: the CB weights or codes at cb
   uint32_t sa[DOWN_ROWS], sb[DOWN_ROWS];  // Q8_0: scales of the blocks holding ca and cb
   if constexpr (FMT == FMT_BF16) {
     const uint16_t* wr = static_cast<const uint16_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
-      wa[r] = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
-      wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+      if constexpr (CA == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
+        wa[r][0] = v.x, wa[r][1] = v.y, wa[r][2] = v.z, wa[r][3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
+        wa[r][0] = v.x, wa[r][1] = v.y;
+      }
+      if constexpr (CB == 2)
+        wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+      else
+        wb[r] = (uint32_t)wr[(size_t)r * DD + cb] << 16;  // the weight in the high half (its FP32 position)
     }
   } else {
     const int8_t* wr = static_cast<const int8_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
     const uint16_t* sr = s_down + (size_t)(DOWN_ROWS * g) * (DD / Q8_BLOCK) + (size_t)s * (D / Q8_BLOCK);
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
-      qa[r] = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
-      wb[r] = *reinterpret_cast<const uint16_t*>(wr + (size_t)r * DD + cb);
+      if constexpr (CA == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
+        wa[r][0] = v.x, wa[r][1] = v.y;
+      } else {
+        wa[r][0] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + ca);
+      }
+      if constexpr (CB == 2)
+        wb[r] = *reinterpret_cast<const uint16_t*>(wr + (size_t)r * DD + cb);
+      else
+        wb[r] = *reinterpret_cast<const uint8_t*>(wr + (size_t)r * DD + cb);
       sa[r] = sr[(size_t)r * (DD / Q8_BLOCK) + ca / Q8_BLOCK];
       sb[r] = sr[(size_t)r * (DD / Q8_BLOCK) + cb / Q8_BLOCK];
     }
@@ -140,25 +170,20 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
     // 2. activations x*w_norm (unscaled) and the lane's sums of squares of this group's tokens
-    float act[TG][10];
+    float act[TG][NC];
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
       const int t = grp * TG + i;
       if (t < T) {
         float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          act[i][e] = xa0[i][e] * na0[e];
-          act[i][4 + e] = xa1[i][e] * na1[e];
-        }
-        act[i][8] = xb[i][0] * nb[0];
-        act[i][9] = xb[i][1] * nb[1];
+        for (int e = 0; e < CA; ++e) act[i][e] = xv[i].a[e] * nv.a[e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa0[i][e], xa0[i][e], ss);
+        for (int e = 0; e < CB; ++e) act[i][CA + e] = xv[i].b[e] * nv.b[e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(xa1[i][e], xa1[i][e], ss);
-        ss = __builtin_fmaf(xb[i][0], xb[i][0], ss);
-        ss = __builtin_fmaf(xb[i][1], xb[i][1], ss);
+        for (int e = 0; e < CA; ++e) ss = __builtin_fmaf(xv[i].a[e], xv[i].a[e], ss);
+#pragma unroll
+        for (int e = 0; e < CB; ++e) ss = __builtin_fmaf(xv[i].b[e], xv[i].b[e], ss);
         v[DOWN_ROWS * T + t] = ss;
       }
     }
@@ -170,22 +195,24 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
     //    (Q8_0: one chain per block chunk, each times its block's scale)
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
-      float wv[10];
+      float wv[NC];
       if constexpr (FMT == FMT_BF16) {
-        const uint32_t u[5] = {wa[r].x, wa[r].y, wa[r].z, wa[r].w, wb[r]};
 #pragma unroll
-        for (int e = 0; e < 5; ++e) {
-          wv[2 * e] = __uint_as_float(u[e] << 16);
-          wv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        for (int e = 0; e < CA / 2; ++e) {
+          wv[2 * e] = __uint_as_float(wa[r][e] << 16);
+          wv[2 * e + 1] = __uint_as_float(wa[r][e] & 0xffff0000u);
+        }
+        if constexpr (CB == 2) {
+          wv[CA] = __uint_as_float(wb[r] << 16);
+          wv[CA + 1] = __uint_as_float(wb[r] & 0xffff0000u);
+        } else {
+          wv[CA] = __uint_as_float(wb[r]);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[e] = code(qa[r].x, e);
-          wv[4 + e] = code(qa[r].y, e);
-        }
-        wv[8] = code(wb[r], 0);
-        wv[9] = code(wb[r], 1);
+        for (int e = 0; e < CA; ++e) wv[e] = code(wa[r][e / 4], e % 4);
+#pragma unroll
+        for (int e = 0; e < CB; ++e) wv[CA + e] = code(wb[r], e);
       }
 #pragma unroll
       for (int i = 0; i < TG; ++i) {
@@ -194,13 +221,15 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
           if constexpr (FMT == FMT_BF16) {
             float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 10; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
+            for (int e = 0; e < NC; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
             v[r * T + t] = acc;
           } else {
             float a8 = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a8 = __builtin_fmaf(wv[e], act[i][e], a8);
-            const float a2 = __builtin_fmaf(wv[9], act[i][9], wv[8] * act[i][8]);
+            for (int e = 0; e < CA; ++e) a8 = __builtin_fmaf(wv[e], act[i][e], a8);
+            float a2 = wv[CA] * act[i][CA];
+#pragma unroll
+            for (int e = 1; e < CB; ++e) a2 = __builtin_fmaf(wv[CA + e], act[i][CA + e], a2);
             v[r * T + t] = __builtin_fmaf(half_bits_to_float(sa[r]), a8, half_bits_to_float(sb[r]) * a2);
           }
         }
@@ -208,16 +237,21 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
     }
   }
 
-  // 4. sums over the wave, then over the 4 waves in a fixed order
+  // 4. sums over the wave, then over the waves in a fixed order
   wave_sum<N>(v);
-  __shared__ float wsum[DOWN_THREADS / 64][N];
+  __shared__ float wsum[DOWN_WAVES][N];
   __shared__ float tot[N];
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) wsum[wave][(lane >> 4) * (N / 4) + i] = v[i];
   }
   __syncthreads();
-  if (tid < N) tot[tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+  if (tid < N) {
+    float a = wsum[0][tid];
+#pragma unroll
+    for (int k = 1; k < DOWN_WAVES; ++k) a += wsum[k][tid];
+    tot[tid] = a;
+  }
   __syncthreads();
 
   // 5. rs of this stream per token, and the rs-scaled partial sums of the 5 rows

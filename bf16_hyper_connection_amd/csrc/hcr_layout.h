@@ -15,11 +15,15 @@ constexpr int R = HCR_RANK;        // down rows = up K
 constexpr int TMAX = HCR_T_MAX;    // tokens per read
 constexpr int DD = S * D;          // 10240: down K = up rows
 
-// ---- down kernel: one work-group = one stream (2,560 columns) x 5 rows of W_down; 4 waves,
-// lane l of wave w owns stream columns [512w + 8l, +8) and [2048 + 128w + 2l, +2)
+// ---- down kernel: one work-group = one stream (2,560 columns) x 5 rows of W_down; 8 waves (two
+// per SIMD), lane l of wave w owns stream columns [256w + 4l, +4) and 2048 + 64w + l
 constexpr int DOWN_ROWS = 5;
 constexpr int DOWN_WGS = S * (R / DOWN_ROWS);  // 256
-constexpr int DOWN_THREADS = 256;
+constexpr int DOWN_WAVES = 8;
+constexpr int DOWN_THREADS = 64 * DOWN_WAVES;
+constexpr int DOWN_CA = 32 / DOWN_WAVES, DOWN_CB = 8 / DOWN_WAVES;  // a lane's columns per row: CA at ca, CB at cb
+static_assert((DOWN_WAVES == 4 || DOWN_WAVES == 8) && DOWN_CA * 64 * DOWN_WAVES == 2048 &&
+              DOWN_CB * 64 * DOWN_WAVES == 512, "the down kernel's column runs must tile the stream");
 // ---- up kernel: one work-group = 10 columns x 4 streams = 40 rows of W_up, 4 waves of 10 rows;
 // a row is reduced by the 32 lanes of a half-wave, lane q owning K [8q, 8q+8) and [256 + 2q, +2)
 constexpr int UP_COLS = 10;

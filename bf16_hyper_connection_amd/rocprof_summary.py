@@ -45,7 +45,17 @@ def kernel_key(name):
         return ("up", int(m.group(1)), int(m.group(4)), m.group(2) == "true", m.group(3) == "true")
     if "hcr::q8_quantize" in name:
         return ("quantize",)
+    m = re.search(r"hcr::mv_bf16<(\d+), (\d+)>", name)
+    if m:
+        return ("matvec", int(m.group(1)), int(m.group(2)))
     return None
+
+
+MV_ROWS, MV_COLS = 12288, 2560
+
+
+def matvec_bytes(T):
+    return MV_ROWS * MV_COLS * 2 + T * MV_COLS * 4 + T * MV_ROWS * 4
 
 
 def _one(pattern, d):
@@ -161,6 +171,19 @@ def main():
         rec["q8_0_quantize"] = {"avg_us": round(dur[q][0], 3), "calls": dur[q][1],
                                 "fetch_KiB": fetch.get(q), "write_KiB": write.get(q)}
 
+    mv_lines = []
+    for T in range(1, 5):
+        k = ("matvec", T, (MV_COLS // 8 + 63) // 64)
+        if k in dur:
+            row = {"avg_us": round(dur[k][0], 3), "calls": dur[k][1], "algorithmic_bytes": matvec_bytes(T),
+                   "algorithmic_GBps": round(matvec_bytes(T) / dur[k][0] / 1e3, 1)}
+            if k in fetch and k in write:
+                row["hbm_bytes"] = int(round(fetch[k] * 1024 * fs + write[k] * 1024 * ws))
+            rec.setdefault("matvec_bf16", {})[str(T)] = row
+            mv_lines.append(f"| {T} | {row['avg_us']:.3f} | {row['algorithmic_GBps']:.0f} | "
+                            + (f"{row['hbm_bytes']:,}" if "hbm_bytes" in row else "—")
+                            + f" | {row['algorithmic_bytes']:,} |")
+
     with open(a.json, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
@@ -195,6 +218,10 @@ def main():
     if q in dur:
         md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
                    f"{dur[q][1]} calls."]
+    if mv_lines:
+        md += ["", f"Skinny BF16 matvec ({MV_ROWS} x {MV_COLS}, 8 rotated copies), `mv_bf16<T, 5>`:", "",
+               "| T | avg µs | algorithmic GB/s | HBM bytes/call (scaled) | algorithmic bytes/call |",
+               "|---|---|---|---|---|"] + mv_lines
     with open(a.md, "w") as fh:
         fh.write("\n".join(md) + "\n")
 
