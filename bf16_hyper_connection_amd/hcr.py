@@ -192,6 +192,7 @@ class HCRead:
         self.device = w_down.device
         self.w_down, self.w_up, self.w_norm = w_down, w_up, w_norm
         self.scratch = torch.empty(hcr_scratch_bytes(), dtype=torch.uint8, device=self.device)
+        self._destroy_fn, self._vp = lib().hcr_destroy, ctypes.c_void_p
 
     @classmethod
     def q8_0(cls, down_codes, down_scales, up_codes, up_scales, w_norm):
@@ -209,9 +210,10 @@ class HCRead:
         return self
 
     def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            hcr_destroy(h)
+        # references bound at creation: at interpreter exit this module's globals may already be gone
+        h, fn, vp = getattr(self, "handle", None), getattr(self, "_destroy_fn", None), getattr(self, "_vp", None)
+        if h and fn is not None and vp is not None:
+            fn(vp(h))
             self.handle = None
 
     def read(self, x, pending=None, inj=None, out=None, mean=None, stream=None):
