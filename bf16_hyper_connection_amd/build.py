@@ -20,16 +20,39 @@ HIPCC_FLAGS = [
 ]
 
 
+def _code_only(text):
+    """C/C++ source without comments and with whitespace collapsed (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
-    """sha256 over the library's sources (csrc/ and include/hcr.h); measurements taken with
-    hardware counters are valid only for the sources they were taken on."""
+    """sha256 over the code of the library's sources (csrc/ and include/hcr.h), comments and whitespace
+    left out; measurements taken with hardware counters are valid only for the code they were taken on."""
     h = hashlib.sha256()
     files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
-    for name in files:
-        with open(os.path.join(CSRC, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
-    with open(os.path.join(ROOT, "include", "hcr.h"), "rb") as fh:
-        h.update(b"hcr.h\0" + fh.read())
+    paths = [os.path.join(CSRC, f) for f in files] + [os.path.join(ROOT, "include", "hcr.h")]
+    for path in paths:
+        with open(path) as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + _code_only(fh.read()).encode() + b"\0")
     return h.hexdigest()
 
 

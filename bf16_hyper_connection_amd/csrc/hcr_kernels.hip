@@ -37,7 +37,10 @@
 //
 // T = 9..16: the down kernel takes the tokens in groups of 8 (the next
 // group's x loads overlap the current group's FMAs); the up kernel streams
-// each token's activations from LDS, so both keep their T <= 8 structure.
+// each token's activations from LDS, so both keep their T <= 8 structure, and
+// a token's result is the same bit for bit at every T (an MFMA path for the
+// larger windows would give those tokens other roundings than the same tokens
+// read in a smaller window).
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
@@ -54,8 +57,9 @@
 // copies of the projections; the block is read as GGML's Q8_0: 32 weights of
 // a row share one binary16 scale d, each weight is d times an int8 code).
 // The same two kernels, templated on the weight format, read int8 codes (half
-// the bytes of BF16) and two scales per lane and row; a lane's 8-column chunk and its 2-column chunk each sit inside one
-// block, so the lane multiplies each chunk's FMA sum by its block's scale.
+// the bytes of BF16) and two scales per lane and row; each of a lane's two
+// column runs sits inside one block, so the lane multiplies each run's FMA sum
+// by its block's scale.
 // The up kernel takes lo in FP32 from LDS (no BF16 split): the codes widen
 // exactly to FP32.  q8_quantize makes the copies on the device: 4 lanes per
 // block, the block maximum over the quad by DPP, then d = amax / 127,

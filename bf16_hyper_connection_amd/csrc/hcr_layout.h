@@ -1,5 +1,6 @@
 // Compile-time geometry, tiling and scratch layout shared by the kernels and the
-// C ABI of the BF16 hyper-connection read.  Host and device code include it.
+// C ABI (the BF16 hyper-connection read, its Q8_0 copies, the skinny matvec).
+// Host and device code include it.
 #pragma once
 
 #include <stddef.h>
@@ -46,8 +47,10 @@ static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0,
 // ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
 enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
 constexpr int Q8_BLOCK = 32;
-static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0,
-              "a lane's 8- and 2-weight chunks must each sit inside one Q8_0 block");
+static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % DOWN_CA == 0 &&
+                  Q8_BLOCK % 8 == 0,
+              "each of a lane's column runs (down: DOWN_CA and DOWN_CB columns; up: 8 and 2) must sit inside one "
+              "Q8_0 block");
 
 // Enqueue the two kernels of one read (T in 1..TMAX; arguments already validated).  For
 // FMT_BF16 the scale pointers are unused.

@@ -191,3 +191,12 @@ def test_matvec_rejects_before_any_hip_call(lib, args, rc):
 
 def test_matvec_empty_is_noop(lib):
     assert hcr.hcr_matvec_bf16(None, 0, 0, 0, None, None, None) == hcr.HCR_OK
+
+
+def test_source_hash_ignores_comments_only():
+    from bf16_hyper_connection_amd import build
+    a = build._code_only('int a = 1;  // note\n/* block\n comment */ int b = 2;')
+    b = build._code_only('int a = 1;\nint b = 2;  /* other */')
+    assert a == b
+    assert build._code_only('const char* s = "// not a comment";') == 'const char* s = "// not a comment";'
+    assert build._code_only("int a = 1;") != build._code_only("int a = 2;")
