@@ -29,18 +29,19 @@
 // projection uses FMA on widened weights instead: its activations change
 // every row group, and the split would cost more VALU than the widening.
 //
-// Why not MFMA: the T <= 8 tokens of the pages' windows fill at most half of a
-// 16-wide MFMA tile, and on MI355X the two-kernel read was measured ~1.5 us
+// Why not MFMA for T <= 9: the pages' windows (T <= 8) fill at most half of
+// a 16-wide MFMA tile, and on MI355X the two-kernel read was measured ~1.5 us
 // slower with v_mfma_f32_16x16x32_bf16 tiles than with this VALU path at
 // T = 1..5 (and within 0.3 us at T = 6..8), the arithmetic being a small part
 // of a latency-bound read.
 //
 // T = 9..16: the down kernel takes the tokens in groups of 8 (the next
-// group's x loads overlap the current group's FMAs); the up kernel streams
-// each token's activations from LDS, so both keep their T <= 8 structure, and
-// a token's result is the same bit for bit at every T (an MFMA path for the
-// larger windows would give those tokens other roundings than the same tokens
-// read in a smaller window).
+// group's x loads overlap the current group's FMAs).  The BF16 up projection
+// of T >= 10 runs on the matrix cores (hc_up_mfma: 16 token columns fill the
+// MFMA tile, and it was measured faster from T = 10); the Q8_0 up kernel
+// streams each token's activations from LDS at every T.  A token's result is
+// the same bit for bit at every T of one range: T = 1..9 and T = 10..16 (the
+// two up kernels round differently).
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
@@ -67,7 +68,8 @@
 // and d stored rounded to binary16.
 //
 // Determinism: every sum has a fixed order, so repeated calls and graph
-// replays are bitwise identical, and each token's result does not depend on T.
+// replays are bitwise identical, and each token's result does not depend on T
+// within T = 1..9 or within T = 10..16.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -456,6 +458,110 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
   }
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+// up: the larger windows (T = UP_MFMA_FROM..16, BF16 weights) on the matrix cores.  The same work-group
+// tile as hc_up (10 columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves 0..2; rows
+// 40..47 are zeros) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K of W_up, B = 32 K x 16 token
+// columns of lo, split into BF16 high and low parts (two MFMAs per K step, high then low, into the same
+// accumulator).  Lane (li, lg) then holds token li of rows 4 lg .. 4 lg + 3 of its tile: the 4 streams
+// of one column, so the epilogue and the stream mean stay in the lane.  Measured on MI355X against the
+// v_dot2 kernel: slower up to T = 9 (the matrix cores cost ~1 us more per launch here), faster from
+// T = 10 (1.4 us per read at T = 16).
+template <int T, bool INJ, bool PEND>
+__global__ __launch_bounds__(UP_THREADS) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
+                                                      const float* __restrict__ part, const float* __restrict__ inj,
+                                                      const float* pending, float* out, float* __restrict__ mean,
+                                                      float* __restrict__ lo_out) {
+  static_assert(T <= 16 && R % 32 == 0 && UP_ROWS <= 48 && UP_THREADS == 256, "3 tiles of 16 rows, 16 tokens");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c0 = blockIdx.x * UP_COLS;
+  const int li = lane & 15, lg = lane >> 4;
+  // 1. small loads first: stream partials and injection for lo, pending for the epilogue
+  constexpr int ITEMS = T * (R / 4);
+  constexpr int NI = (ITEMS + UP_THREADS - 1) / UP_THREADS;
+  f32x4 pv[NI][S], iv[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it = tid + n * UP_THREADS;
+    if (it < ITEMS) {
+      const int t = it / (R / 4), k = 4 * (it % (R / 4));
+#pragma unroll
+      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
+      if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
+    }
+  }
+  // epilogue lane: token li, column cc = 4 * wave + lg (valid when wave < 3, cc < 10, li < T)
+  const int cc = 4 * wave + lg;
+  const bool eok = wave < 3 && cc < UP_COLS && li < T;
+  float pend[S] = {0.f, 0.f, 0.f, 0.f};
+  if (PEND && eok) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) pend[s] = pending[((size_t)li * S + s) * D + c0 + cc];
+  }
+  // 2. weights (A operand): tile = wave, row rw = 16 * wave + li (rows past 40 are zeros), K 32 m + 8 lg
+  const int rw = 16 * wave + li;
+  const bool wok = wave < 3 && rw < UP_ROWS;
+  const uint16_t* row = static_cast<const uint16_t*>(w_up) + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
+  uint4 a[R / 32];
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m)
+    a[m] = wok ? *reinterpret_cast<const uint4*>(row + 32 * m + 8 * lg) : make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order:
+  //    bh[m][g][t] = high parts of lo[t][32 m + 8 g .. + 8] (zeros for tokens t >= T)
+  __shared__ __attribute__((aligned(16))) float lo_sm[T * R];
+  __shared__ uint4 bh[R / 32][4][16], bl[R / 32][4][16];
+  __shared__ float gate_sm[T][S];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it = tid + n * UP_THREADS;
+    if (it < ITEMS) {
+      const int t = it / (R / 4), k = 4 * (it % (R / 4));
+      f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
+      if (INJ) vv += iv[n];
+      *reinterpret_cast<f32x4*>(lo_sm + t * R + k) = vv;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < (R / 32) * 4 * 16; i += UP_THREADS) {
+    const int t = i & 15, g = (i >> 4) & 3, m = i >> 6;
+    float v8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v8[e] = t < T ? lo_sm[t * R + 32 * m + 8 * g + e] : 0.f;
+    uint4 hi, lo;
+    split_hi_lo(v8, hi, lo);
+    bh[m][g][t] = hi;
+    bl[m][g][t] = lo;
+  }
+  if (tid < T * S) gate_sm[tid / S][tid % S] = 1.0f / (1.0f + expf(-lo_sm[(tid / S) * R + (tid % S)]));
+  if (blockIdx.x == 0)
+    for (int i = tid; i < T * R; i += UP_THREADS) lo_out[i] = lo_sm[i];
+  __syncthreads();
+  if (wave >= 3) return;
+  // 4. the tile on the matrix cores, K in order, high part then low part of each step
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bh[m][lg][li]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bl[m][lg][li]), acc, 0, 0, 0);
+  }
+  // 5. epilogue: lane = token li, rows 16 wave + 4 lg + s = stream s of column 4 wave + lg; the stream
+  //    mean in the v_dot2 kernel's order ((s0 + s1) + (s2 + s3))
+  if (eok) {
+    float o[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      o[s] = gate_sm[li][s] * acc[s];
+      if (PEND) o[s] += pend[s];
+      out[((size_t)li * S + s) * D + c0 + cc] = o[s];
+    }
+    mean[(size_t)li * D + c0 + cc] = 0.25f * ((o[0] + o[1]) + (o[2] + o[3]));
+  }
+}
+
+
 // ---------------------------------------------------------------------------
 // Q8_0 copies on the device: 4 lanes per 32-weight block (8 BF16 weights each);
 // each lane takes Q8_CHUNKS chunks a grid-stride apart, all loads issued first
@@ -534,6 +640,13 @@ static const up_fn kUp[2][TMAX][2][2] = {HCR_UP_ROW(FMT_BF16), HCR_UP_ROW(FMT_Q8
 #undef HCR_UP_ROW
 #undef HCR_UP_T
 
+#define HCR_UPM_T(T) {{hc_up_mfma<T, false, false>, hc_up_mfma<T, false, true>}, \
+                      {hc_up_mfma<T, true, false>, hc_up_mfma<T, true, true>}}
+static_assert(UP_MFMA_FROM == 10 && TMAX == 16, "the table below lists T = 10..16");
+static const up_fn kUpM[TMAX - UP_MFMA_FROM + 1][2][2] = {HCR_UPM_T(10), HCR_UPM_T(11), HCR_UPM_T(12), HCR_UPM_T(13),
+                                                          HCR_UPM_T(14), HCR_UPM_T(15), HCR_UPM_T(16)};
+#undef HCR_UPM_T
+
 int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, const void* w_up, const uint16_t* s_up,
                 const float* w_norm, void* scratch, const float* x, const float* pending, const float* inj,
                 float* out, float* mean, void* stream) {
@@ -545,8 +658,9 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
   hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, w_down, s_down, x, w_norm, part,
                      rs);
-  hipLaunchKernelGGL(kUp[fmt][T - 1][inj != nullptr][pending != nullptr], dim3(UP_WGS), dim3(UP_THREADS), 0, st,
-                     w_up, s_up, part, inj, pending, out, mean, lo);
+  const up_fn up = fmt == FMT_BF16 && T >= UP_MFMA_FROM ? kUpM[T - UP_MFMA_FROM][inj != nullptr][pending != nullptr]
+                                                        : kUp[fmt][T - 1][inj != nullptr][pending != nullptr];
+  hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(UP_THREADS), 0, st, w_up, s_up, part, inj, pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }
 

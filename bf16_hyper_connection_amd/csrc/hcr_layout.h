@@ -33,6 +33,7 @@ constexpr int UP_THREADS = 256;
 constexpr int UP_ROWS = UP_COLS * S;                         // 40
 constexpr int UP_WAVE_ROWS = UP_ROWS / (UP_THREADS / 64);    // 10
 constexpr int UP_ITERS = UP_WAVE_ROWS / 2;                   // 5 (two rows per iteration, one per half-wave)
+constexpr int UP_MFMA_FROM = 10;  // BF16 up projection of T >= 10 on the matrix cores (measured faster there)
 
 // ---- scratch (bytes) ----
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }

@@ -18,8 +18,12 @@
  *   mean[t,c]  = (1/4) * sum_s out[t,s,c]
  *
  * T may be 0..16 (the pages' windows are 1..8 tokens; 9..16 serve larger windows).
- * Arithmetic is FP32 (BF16 weights are widened exactly); summation orders
- * are fixed, so a call is bitwise reproducible, also as a replayed HIP graph.
+ * Arithmetic is FP32 (BF16 weights are widened exactly; for T >= 10 the up
+ * projection of BF16 weights runs on the matrix cores with lo split into BF16
+ * high and low parts); summation orders are fixed, so a call is bitwise
+ * reproducible, also as a replayed HIP graph, and a token's results are the same
+ * bit for bit whatever the other tokens of the window, within T = 1..9 and
+ * within T = 10..16.
  *
  * Memory. Every pointer is a device pointer the caller owns (the library
  * allocates nothing on the device and never frees caller memory).  Layouts

@@ -184,9 +184,9 @@ def test_repeated_reads_bitwise(wset):
     assert torch.equal(o, o0) and torch.equal(m, m0)
 
 
-@pytest.mark.parametrize("T", [8, 16])
+@pytest.mark.parametrize("T", [8, 9])
 def test_token_results_do_not_depend_on_T(wset, T):
-    """Each token's result is the same, bit for bit, whether it is read alone or in a window of T."""
+    """T = 1..9 (v_dot2 up kernel): each token's result is the same, bit for bit, read alone or in a window of T."""
     w, reader = wset
     x, p, inj = gen.activations(8, T), gen.pending(8, T), gen.injection(8, T)
     o8, m8 = _read(reader, x, p, inj)
@@ -195,6 +195,20 @@ def test_token_results_do_not_depend_on_T(wset, T):
         o1, m1 = _read(reader, x[t:t + 1], p[t:t + 1], inj[t:t + 1])
         torch.cuda.synchronize()
         assert torch.equal(o1[0], o8[t]) and torch.equal(m1[0], m8[t]), f"token {t}"
+
+
+def test_token_results_do_not_depend_on_T_in_the_larger_windows(wset):
+    """T = 10..16 (matrix-core up kernel): each token of a 16-token read equals the same token in windows of
+    10..15 tokens, bit for bit."""
+    w, reader = wset
+    T = 16
+    x, p, inj = gen.activations(18, T), gen.pending(18, T), gen.injection(18, T)
+    o16, m16 = _read(reader, x, p, inj)
+    o16, m16 = o16.clone(), m16.clone()
+    for a, b in ((0, 10), (6, 16), (2, 15), (3, 14)):
+        o, m = _read(reader, x[a:b], p[a:b], inj[a:b])
+        torch.cuda.synchronize()
+        assert torch.equal(o, o16[a:b]) and torch.equal(m, m16[a:b]), f"tokens {a}..{b - 1}"
 
 
 def test_numerics_stress_graph_replay_bitwise():
