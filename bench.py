@@ -175,6 +175,26 @@ def main():
         log(f"bench: T={T} {us:.3f} us/read  {per_T_gbps[T]:.0f} GB/s")
         del g
 
+    # cold-cache check: T = 1 and T = 8 with 1 weight set (MALL- and L2-resident), the 32 sets, and 64 sets
+    # (the 32 and copies of them in other memory); 32 and 64 must agree if the rotation defeats the MALL
+    extra = [hcr.HCRead(r.w_down.clone(), r.w_up.clone(), r.w_norm.clone()) for r in readers]
+    cold_check = {}
+    for T in (1, TMAX):
+        row = {}
+        for name, pool in (("1_set", readers[:1] * len(readers)), ("32_sets", readers), ("64_sets", readers + extra)):
+            gc = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(gc, stream=stream):
+                    for r in pool:
+                        r.read(xs[T], out=outs[T], mean=means[T])
+            torch.cuda.current_stream().wait_stream(stream)
+            row[name] = round(timed(gc, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(pool)), 3)
+            del gc
+        cold_check[T] = row
+        log(f"bench: cold check T={T}: {row}")
+    del extra
+
     # the timed steps: the whole sweep per step
     g = capture(range(1, TMAX + 1), len(readers))
     reads_per_step = TMAX * len(readers)
@@ -354,6 +374,7 @@ def main():
                                           "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items()
                                                                      if T > TMAX},
                                           "note": "same cold rotation, not part of the timed step"},
+                   "cold_cache_check_us_per_read": cold_check,
                    "verify_window": window, "q8_0": q8, "matvec_bf16": matvec},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,

@@ -1,5 +1,5 @@
-// C ABI of the BF16 hyper-connection read: argument validation and the handle.
-// Every check runs on the host before any HIP call.
+// C ABI of the BF16 hyper-connection read, its Q8_0 copies and the skinny BF16 matvec: argument
+// validation and the handle.  Every check runs on the host before any HIP call.
 
 #include <stdint.h>
 #include <stdlib.h>

@@ -95,7 +95,9 @@ def timed_region(trace_dir):
         dur[kernel_key(r["Kernel_Name"])[0]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     reads = len(dur["down"])
     span = (max(int(r["End_Timestamp"]) for r in region) - min(int(r["Start_Timestamp"]) for r in region)) / 1000.0
-    return reads, span / reads, statistics.mean(dur["down"]), statistics.mean(dur["up"])
+    per_read = sorted(d + u for d, u in zip(dur["down"], dur["up"]))
+    pct = {p: per_read[min(len(per_read) - 1, int(p / 100.0 * len(per_read)))] for p in (10, 50, 90)}
+    return reads, span / reads, statistics.mean(dur["down"]), statistics.mean(dur["up"]), pct
 
 
 def counters(d, counter):
@@ -168,7 +170,8 @@ def main():
     tr = timed_region(a.trace)
     if tr:
         rec["timed_region"] = {"reads": tr[0], "us_per_read": round(tr[1], 3), "down_avg_us": round(tr[2], 3),
-                               "up_avg_us": round(tr[3], 3)}
+                               "up_avg_us": round(tr[3], 3),
+                               "down_plus_up_us_p10_p50_p90": [round(tr[4][p], 3) for p in (10, 50, 90)]}
     q = ("quantize",)
     if q in dur:
         rec["q8_0_quantize"] = {"avg_us": round(dur[q][0], 3), "calls": dur[q][1],
@@ -213,7 +216,8 @@ def main():
         tot = tr[2] + tr[3]
         md += ["", f"Timed region of the traced bench run (its timed steps, found between two marker kernels): "
                    f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + hc_up {tr[3]:.3f} µs = "
-                   f"{tot:.3f} µs per read."
+                   f"{tot:.3f} µs per read (p10 / p50 / p90 of down + up per read: "
+                   f"{tr[4][10]:.3f} / {tr[4][50]:.3f} / {tr[4][90]:.3f} µs)."
                    + (f" An untraced `python bench.py` of the same session measured {untraced:.3f} µs per read "
                       f"event-timed (its `value`; {100 * tot / untraced - 100:+.1f} %)." if untraced else "")
                    + (f" Under the tracer the dispatches are spaced out: the traced run's own event figure is "
