@@ -203,6 +203,14 @@ def matvec_weights(base, index=0, rows=MV_ROWS, cols=MV_COLS):
     return f32_to_bf16_bits(w)
 
 
+def matvec_int_weights(base, rows, cols, index=0):
+    """W = k / 16 with k uniform in -8..8, as BF16 bits [rows][cols] (exact in BF16; cheap to draw for very
+    tall matrices)."""
+    k = rng(base, _P_MV_W, index).integers(-8, 9, size=rows * cols, dtype=np.int8)
+    w = k.astype(np.float32) * np.float32(0.0625)
+    return (w.view(np.uint32) >> np.uint32(16)).astype(np.uint16).reshape(rows, cols)
+
+
 def matvec_x(base, T, index=0, cols=MV_COLS):
     """x ~ N(0, 1), float32 [T][cols]."""
     return rng(base, _P_MV_X, index).standard_normal((T, cols), dtype=np.float32)

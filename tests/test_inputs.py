@@ -69,3 +69,10 @@ def test_q8_edge_weights_are_seeded_and_cover_every_family():
     assert not np.any(blocks[1::n])                               # the all-zero family
     assert np.all(np.count_nonzero(blocks[2::n], axis=1) == 1)   # one nonzero entry
     assert not np.array_equal(a, gen.q8_edge_weights(4))
+
+
+def test_matvec_int_weights_exact_in_bf16():
+    w = gen.matvec_int_weights(3, 10, 16)
+    f = (w.astype(np.uint32) << 16).view(np.float32)
+    assert w.shape == (10, 16) and np.all(np.abs(f) <= 0.5) and np.all(f * 16 == np.round(f * 16))
+    assert np.array_equal(w, gen.matvec_int_weights(3, 10, 16))

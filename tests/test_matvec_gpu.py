@@ -94,3 +94,16 @@ def test_matvec_graph_replay_bitwise(full_w):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, direct), f"replay {i}"
+
+
+@pytest.mark.parametrize("rows", [1_048_577, 1_100_003])
+def test_matvec_tall_matrix_walks_the_grid_in_steps(rows):
+    """More row groups than the grid's 65,536 work-groups of 4 waves hold (262,144 groups of 4 rows): the
+    waves take a second step (1,048,577 rows: exactly one group in the second step)."""
+    cols, T = 8, 2
+    w = gen.matvec_int_weights(25, rows, cols)
+    x = gen.matvec_x(25, T, cols=cols)
+    y = hcr.matvec_bf16(to_dev(w), to_dev(x))
+    torch.cuda.synchronize()
+    e = max_rel(y, oracle.matvec_bf16(w, x))
+    assert e <= TOL, f"tall matrix: error {e:.3e}"

@@ -163,3 +163,19 @@ def test_q8_quantize_in_a_graph_bitwise():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(codes, c0) and torch.equal(scales, s0), f"replay {i}"
+
+
+def test_q8_residual_chain_of_16_reads():
+    """A verify-window chain on Q8_0 copies: 16 reads, out_i = x_{i+1}, T = 6, pending on; each step against the
+    reference on the x the GPU fed it."""
+    n, T = 16, 6
+    c = gen.verify_window(n, T, base=19)
+    sets = [Q8Set(w) for w in c["weights"]]
+    x = to_dev(c["x0"])
+    x_host = c["x0"]
+    for i, s in enumerate(sets):
+        out, mean = s.reader.read(x, to_dev(c["pending"][i]))
+        torch.cuda.synchronize()
+        ref = s.ref_read(x_host, c["pending"][i])
+        check_read(s.reader, T, out, mean, ref, f"Q8_0 chain step {i}")
+        x, x_host = out, out.cpu().numpy()
