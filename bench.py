@@ -245,7 +245,7 @@ def main():
         del gq
         q_bytes = R * S * D * (2 + 1) + R * S * D // 32 * 2  # BF16 read, codes and scales written
         q8_T_us, q8_T_gbps = {}, {}
-        for T in range(1, TMAX + 1):
+        for T in range(1, T_WIDE + 1):
             gq = torch.cuda.CUDAGraph()
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
@@ -258,7 +258,7 @@ def main():
             q8_T_gbps[T] = round(algorithmic_bytes_q8(T) / us / 1e3, 1)
             log(f"bench: Q8_0 T={T} {us:.3f} us/read  {q8_T_gbps[T]:.0f} GB/s")
             del gq
-        mean_us = sum(q8_T_us.values()) / TMAX
+        mean_us = sum(q8_T_us[T] for T in range(1, TMAX + 1)) / TMAX
         mean_bytes = sum(algorithmic_bytes_q8(T) for T in range(1, TMAX + 1)) / TMAX
         q8 = {"per_T_us": q8_T_us, "per_T_algorithmic_GBps": q8_T_gbps, "mean_us_T1_8": round(mean_us, 3),
               "weight_sets": len(q8_readers), "weight_bytes_per_read": algorithmic_bytes_q8(0) - S * D * 4,
