@@ -1,4 +1,5 @@
-"""Build libhcr.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc."""
+"""Build libhcr.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc, and the plain C
+caller of the ABI that the tests run (tests/c_caller/hcr_read_file, built with the host C compiler)."""
 
 import hashlib
 import os
@@ -10,6 +11,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhcr.so")
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller", "hcr_read_file.c")
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "hcr_read_file")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# C11 with every warning an error: include/hcr.h must stay plain C
+C_FLAGS = ["-std=c11", "-O2", "-Wall", "-Wextra", "-Wpedantic", "-Werror",
+           "-D__HIP_PLATFORM_AMD__"]  # selects the AMD half of the HIP runtime header
 
 SOURCES = ["hcr_kernels.hip", "hcr_matvec.hip", "hcr_api.cpp"]
 HIPCC_FLAGS = [
@@ -63,8 +70,33 @@ def hipcc():
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+def c_compiler():
+    for cand in (os.environ.get("CC"), shutil.which("gcc"), shutil.which("cc")):
+        if cand and shutil.which(cand):
+            return cand
+    raise RuntimeError("no host C compiler (gcc or cc): the C caller cannot be built")
+
+
+def build_c_caller(verbose=False):
+    """Compile the C caller against include/hcr.h and link it to the built libhcr.so and the HIP
+    runtime; returns its path."""
+    tmp = C_CALLER + ".tmp%d" % os.getpid()
+    cmd = [c_compiler()] + C_FLAGS + ["-I", os.path.join(ROOT, "include"), "-isystem", os.path.join(ROCM, "include"),
+           C_CALLER_SRC, "-o", tmp, "-L", PKG, "-lhcr", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + os.path.relpath(PKG, os.path.dirname(C_CALLER)).join(["$ORIGIN/", ""]),
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("the C caller did not compile:\n" + res.stdout + res.stderr)
+    os.replace(tmp, C_CALLER)
+    return C_CALLER
+
+
 def build(verbose=False):
-    """Compile every source into libhcr.so (always recompiles); returns the library path."""
+    """Compile every source into libhcr.so, then the C caller (always recompiles); returns the
+    library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + \
           [os.path.join(CSRC, s) for s in SOURCES]
@@ -78,6 +110,7 @@ def build(verbose=False):
     if verbose and out.strip():
         print(out, flush=True)
     os.replace(tmp, LIB)
+    build_c_caller(verbose)
     return LIB
 
 

@@ -184,6 +184,35 @@ def test_repeated_reads_bitwise(wset):
     assert torch.equal(o, o0) and torch.equal(m, m0)
 
 
+def test_distinct_handles_on_two_streams():
+    """Two handles (two weight sets, each with its own scratch) reading at the same time on two streams:
+    every result equals the same read made alone, bit for bit."""
+    sets = [gen.weight_set(30, k) for k in range(2)]
+    readers = [reader_for(w) for w in sets]
+    T = (5, 12)
+    xs = [to_dev(gen.activations(31, T[k], index=k)) for k in range(2)]
+    ps = [to_dev(gen.pending(31, T[k], index=k)) for k in range(2)]
+    ij = [to_dev(gen.injection(31, T[k], index=k)) for k in range(2)]
+    alone = []
+    for k in range(2):
+        o, m = readers[k].read(xs[k], ps[k], ij[k])
+        torch.cuda.synchronize()
+        alone.append((o.clone(), m.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = [[None] * 2 for _ in range(20)]
+    for i in range(20):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                outs[i][k] = readers[k].read(xs[k], ps[k], ij[k])
+    torch.cuda.synchronize()
+    for i in range(20):
+        for k in range(2):
+            o, m = outs[i][k]
+            assert torch.equal(o, alone[k][0]) and torch.equal(m, alone[k][1]), f"round {i} handle {k}"
+
+
 @pytest.mark.parametrize("T", [8, 9])
 def test_token_results_do_not_depend_on_T(wset, T):
     """T = 1..9 (v_dot2 up kernel): each token's result is the same, bit for bit, read alone or in a window of T."""
