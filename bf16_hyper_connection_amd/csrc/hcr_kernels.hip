@@ -16,32 +16,38 @@
 //     (halving with v_permlane32/16_swap, then DPP) and over the 8 waves (LDS,
 //     fixed order); the work-group writes rs[t][s] * (row sums), one partial
 //     per stream.
-//   hc_up<T, INJ, PEND>: lo[t][k] = the 4 stream partials (+ injection), then
-//     40 rows of W_up (10 columns x 4 streams) per work-group.  Each row is
-//     reduced by the 32 lanes of a half-wave; lane q owns K [8q, 8q+8) and
-//     [256+2q, +2) and multiplies with v_dot2_f32_bf16 against lo split into
-//     BF16 high and low parts.  Epilogue: pending write, sigmoid gate of
-//     lo[t][s], stream mean of 4 adjacent outputs (DPP quad).
+//   hc_up_mfma<T, INJ, PEND> (BF16 weights, T >= 2): lo[t][k] = the 4 stream
+//     partials (+ injection), then 40 rows of W_up (10 columns x 4 streams) per
+//     work-group as three 16-row tiles on the matrix cores
+//     (v_mfma_f32_16x16x32_bf16), lo split into BF16 high and low parts as the
+//     B operand.  Up to 8 tokens the high parts fill B columns 0..7 and the low
+//     parts columns 8..15, one product per K step; from 9 tokens each part has
+//     its own product.  Epilogue in the lane: pending write, sigmoid gate of
+//     lo[t][s], stream mean.
+//   hc_up<T, INJ, PEND>: the same tile on the vector ALUs (BF16 at T = 1, and
+//     every Q8_0 read).  Each row is reduced by the 32 lanes of a half-wave;
+//     lane q owns K [8q, 8q+8) and [256+2q, +2) and multiplies with
+//     v_dot2_f32_bf16 against the high and low parts of lo.  Epilogue: pending
+//     write, sigmoid gate, stream mean of 4 adjacent outputs (DPP quad).
 //
-// Why v_dot2 on high/low parts of lo: the activations are FP32.  Rounding lo
-// to BF16 once loses ~2^-9 relative, above the read's 1e-4 tolerance; the
-// high part plus the BF16-rounded remainder keep ~2^-17.  The down
-// projection uses FMA on widened weights instead: its activations change
-// every row group, and the split would cost more VALU than the widening.
+// Why the high/low split of lo: the activations are FP32.  Rounding lo to
+// BF16 once loses ~2^-9 relative, above the read's 1e-4 tolerance; the high
+// part plus the BF16-rounded remainder keep ~2^-17.  The down projection uses
+// FMA on widened weights instead: its activations change every row group, and
+// the split would cost more VALU than the widening.
 //
-// Why not MFMA for T <= 9: the pages' windows (T <= 8) fill at most half of
-// a 16-wide MFMA tile, and on MI355X the two-kernel read was measured ~1.5 us
-// slower with v_mfma_f32_16x16x32_bf16 tiles than with this VALU path at
-// T = 1..5 (and within 0.3 us at T = 6..8), the arithmetic being a small part
-// of a latency-bound read.
+// Why the matrix cores for the up projection from T = 2: the v_dot2 kernel
+// issues ~100 VALU instructions per token per wave, which the loads cannot
+// hide with one wave per SIMD; the matrix-core kernel's 10 or 20 MFMAs per
+// wave cost the same at every T.  Measured on MI355X, whole read: T = 1
+// 7.03 us (v_dot2) against 7.21 (matrix cores), T = 2 7.60 against 7.56,
+// T = 8 10.42 against 9.28.
 //
 // T = 9..16: the down kernel takes the tokens in groups of 8 (the next
-// group's x loads overlap the current group's FMAs).  The BF16 up projection
-// of T >= 10 runs on the matrix cores (hc_up_mfma: 16 token columns fill the
-// MFMA tile, and it was measured faster from T = 10); the Q8_0 up kernel
-// streams each token's activations from LDS at every T.  A token's result is
-// the same bit for bit at every T of one range: T = 1..9 and T = 10..16 (the
-// two up kernels round differently).
+// group's x loads overlap the current group's FMAs).  A token's result is the
+// same bit for bit at every T of one range: T = 2..8 and T = 9..16 (the two
+// B layouts round differently); a token read alone (T = 1, v_dot2) rounds
+// differently again.
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
@@ -69,7 +75,7 @@
 //
 // Determinism: every sum has a fixed order, so repeated calls and graph
 // replays are bitwise identical, and each token's result does not depend on T
-// within T = 1..9 or within T = 10..16.
+// within T = 2..8 or within T = 9..16 (BF16), or within T = 1..16 (Q8_0).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -270,6 +276,45 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 }
 
 
+// The up kernels' first loads: the 4 stream partials (and the injection) of lo, 4 K values of one token
+// per item, items tid + n * NT (NT threads).  Neither the loads nor the stores of lo are conditional: items
+// past the end repeat the last item (the same value to the same LDS address).  A branch among the loads
+// makes the compiler wait for every load issued so far, and a branch around their only use lets it sink
+// them below the weight loads; either would serialise them with the weight stream.
+template <int T, bool INJ, int NI, int NT>
+__device__ __forceinline__ void load_partials(int tid, const float* __restrict__ part,
+                                              const float* __restrict__ inj, f32x4 (&pv)[NI][S],
+                                              f32x4 (&iv)[NI]) {
+  constexpr int ITEMS = T * (R / 4);
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it = min(tid + n * NT, ITEMS - 1);
+    const int t = it / (R / 4), k = 4 * (it % (R / 4));
+#pragma unroll
+    for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
+    if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
+  }
+}
+
+// lo[t][k] = ((p0 + p1) + p2) + p3 (+ inj) into LDS, for the items load_partials loaded.  lo_sm holds
+// T * R + LO_JUNK floats: a lane past the last item stores its repeat into its own slot after lo (the
+// address is selected, not branched on), so that no two lanes of a wave write one LDS address.
+constexpr int LO_JUNK = 64 * 4;
+template <int T, bool INJ, int NI, int NT>
+__device__ __forceinline__ void store_lo(int tid, const f32x4 (&pv)[NI][S], const f32x4 (&iv)[NI],
+                                         float* lo_sm) {
+  constexpr int ITEMS = T * (R / 4);
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it = min(tid + n * NT, ITEMS - 1);
+    const int t = it / (R / 4), k = 4 * (it % (R / 4));
+    f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
+    if (INJ) vv += iv[n];
+    const int at = tid + n * NT < ITEMS ? t * R + k : T * R + 4 * (tid & 63);
+    *reinterpret_cast<f32x4*>(lo_sm + at) = vv;
+  }
+}
+
 // up: lo = sum of the 4 stream partials (+ injection); 40 rows of W_up (10 columns x 4 streams) per work-group
 template <int T, bool INJ, bool PEND, int FMT>
 __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_up,
@@ -287,28 +332,17 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
   constexpr int ITEMS = T * (R / 4);  // (token, 4 K values)
   constexpr int NI = (ITEMS + UP_THREADS - 1) / UP_THREADS;
   f32x4 pv[NI][S], iv[NI];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int it = tid + n * UP_THREADS;
-    if (it < ITEMS) {
-      const int t = it / (R / 4), k = 4 * (it % (R / 4));
-#pragma unroll
-      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
-      if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
-    }
-  }
+  load_partials<T, INJ, NI, UP_THREADS>(tid, part, inj, pv, iv);
   // epilogue: output o = (t * UP_COLS + cc) * 4 + s, the 4 streams of a column in an aligned quad of lanes
   constexpr int NO = (T * UP_ROWS + UP_THREADS - 1) / UP_THREADS;
   float pend[NO];
 #pragma unroll
   for (int n = 0; n < NO; ++n) {
-    const int o = tid + n * UP_THREADS;
-    pend[n] = 0.f;
-    if (PEND && o < T * UP_ROWS) {
-      const int t = o / UP_ROWS, cc = (o / S) % UP_COLS, s = o % S;
-      pend[n] = pending[((size_t)t * S + s) * D + c0 + cc];
-    }
+    const int o = min(tid + n * UP_THREADS, T * UP_ROWS - 1);  // clamped: no branch among the loads
+    const int t = o / UP_ROWS, cc = (o / S) % UP_COLS, s = o % S;
+    pend[n] = PEND ? pending[((size_t)t * S + s) * D + c0 + cc] : 0.f;
   }
+  __builtin_amdgcn_sched_barrier(0);  // keeps every small load ahead of the weight loads
 
   // 2. weights: iteration m, half h -> row rw = 10*wave + 2m + h (column rw >> 2, stream rw & 3);
   //    lane q owns K [8q, 8q+8) (one 16-byte chunk) and [256 + 2q, 256 + 2q + 2) (one dword)
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  __shared__ __attribute__((aligned(16))) float lo_sm[T * R];
+  __shared__ __attribute__((aligned(16))) float lo_sm[T * R + LO_JUNK];
   constexpr int TS = FMT == FMT_BF16 ? T : 1;  // the BF16 split of lo; Q8_0 reads lo itself
   __shared__ uint4 acta_sm[2][TS][32];  // K [8q, 8q+8): high, low parts
   __shared__ uint2 actb_sm[TS][32];     // K [256+2q, +2): (high, low)
@@ -342,16 +376,7 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
   __shared__ float u_sm[T][UP_ROWS];
 
   // 3. lo[t][k] = ((p0 + p1) + p2) + p3 (+ inj)
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int it = tid + n * UP_THREADS;
-    if (it < ITEMS) {
-      const int t = it / (R / 4), k = 4 * (it % (R / 4));
-      f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
-      if (INJ) vv += iv[n];
-      *reinterpret_cast<f32x4*>(lo_sm + t * R + k) = vv;
-    }
-  }
+  store_lo<T, INJ, NI, UP_THREADS>(tid, pv, iv, lo_sm);
   __syncthreads();
   // 4. lo as BF16 high/low v_dot2 operands, in each lane's K order; gates; lo for inspection
   for (int i = tid; FMT == FMT_BF16 && i < T * 32; i += UP_THREADS) {
@@ -460,92 +485,94 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-// up: the larger windows (T = UP_MFMA_FROM..16, BF16 weights) on the matrix cores.  The same work-group
-// tile as hc_up (10 columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves 0..2; rows
-// 40..47 are zeros) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K of W_up, B = 32 K x 16 token
-// columns of lo, split into BF16 high and low parts (two MFMAs per K step, high then low, into the same
-// accumulator).  Lane (li, lg) then holds token li of rows 4 lg .. 4 lg + 3 of its tile: the 4 streams
-// of one column, so the epilogue and the stream mean stay in the lane.  Measured on MI355X against the
-// v_dot2 kernel: slower up to T = 9 (the matrix cores cost ~1 us more per launch here), faster from
-// T = 10 (1.4 us per read at T = 16).
+// up on the matrix cores (BF16 weights, T = UP_MFMA_FROM..16).  The same work-group tile as hc_up (10
+// columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves 0..2; rows 40..47 repeat row 39
+// and are not stored) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K of W_up, B = 32 K x 16 columns
+// of lo split into BF16 high and low parts.  T <= 8: column t holds token t's high parts and column
+// 8 + t its low parts (one MFMA per K step); T > 8: one B matrix of high parts and one of low parts
+// (two MFMAs per K step, high then low, into the same accumulator).  Lane (li, lg) then holds column li
+// of rows 4 lg .. 4 lg + 3 of its tile: the 4 streams of one output column, so the epilogue and the
+// stream mean stay in the lane (T <= 8: after adding column li + 8 by a row rotation).
 template <int T, bool INJ, bool PEND>
-__global__ __launch_bounds__(UP_THREADS) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
-                                                      const float* __restrict__ part, const float* __restrict__ inj,
-                                                      const float* pending, float* out, float* __restrict__ mean,
-                                                      float* __restrict__ lo_out) {
-  static_assert(T <= 16 && R % 32 == 0 && UP_ROWS <= 48 && UP_THREADS == 256, "3 tiles of 16 rows, 16 tokens");
+__global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
+                                                  const float* __restrict__ part, const float* __restrict__ inj,
+                                                  const float* pending, float* out, float* __restrict__ mean,
+                                                  float* __restrict__ lo_out) {
+  constexpr int UPM_THREADS = upm_threads(T);
+  static_assert(T <= 16 && R % 32 == 0 && UP_ROWS > 32 && UP_ROWS <= 48 && (UPM_THREADS == 192 || UPM_THREADS == 256),
+                "3 tiles of 16 rows (waves 0..2), 16 token columns");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = blockIdx.x * UP_COLS;
   const int li = lane & 15, lg = lane >> 4;
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue
   constexpr int ITEMS = T * (R / 4);
-  constexpr int NI = (ITEMS + UP_THREADS - 1) / UP_THREADS;
+  constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int it = tid + n * UP_THREADS;
-    if (it < ITEMS) {
-      const int t = it / (R / 4), k = 4 * (it % (R / 4));
-#pragma unroll
-      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
-      if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
-    }
-  }
-  // epilogue lane: token li, column cc = 4 * wave + lg (valid when wave < 3, cc < 10, li < T)
+  load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
+  // epilogue lane: token li, column cc = 4 * wave + lg (valid when wave < 3, cc < 10 and li < T); the
+  // pending loads are clamped to a valid (token, column), so that no branch separates the loads
   const int cc = 4 * wave + lg;
   const bool eok = wave < 3 && cc < UP_COLS && li < T;
-  float pend[S] = {0.f, 0.f, 0.f, 0.f};
-  if (PEND && eok) {
+  float pend[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) pend[s] = pending[((size_t)li * S + s) * D + c0 + cc];
-  }
-  // 2. weights (A operand): tile = wave, row rw = 16 * wave + li (rows past 40 are zeros), K 32 m + 8 lg
-  const int rw = 16 * wave + li;
-  const bool wok = wave < 3 && rw < UP_ROWS;
+  for (int s = 0; s < S; ++s)
+    pend[s] = PEND ? pending[((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1)] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);  // keeps every small load ahead of the weight loads
+  // 2. weights (A operand): tile = wave, row rw = 16 * wave + li, K 32 m + 8 lg.  No load is conditional:
+  //    rows 40..47 of the third tile re-load row 39, and a 4th wave (T >= 10) re-loads the third tile's
+  //    rows, cache hits whose results are never stored.  A branch around loads, even a wave-uniform one,
+  //    makes the compiler wait for them before the first barrier, serialising the weight stream with the
+  //    lo staging.
+  const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
   const uint16_t* row = static_cast<const uint16_t*>(w_up) + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
   uint4 a[R / 32];
 #pragma unroll
-  for (int m = 0; m < R / 32; ++m)
-    a[m] = wok ? *reinterpret_cast<const uint4*>(row + 32 * m + 8 * lg) : make_uint4(0, 0, 0, 0);
+  for (int m = 0; m < R / 32; ++m) a[m] = *reinterpret_cast<const uint4*>(row + 32 * m + 8 * lg);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order:
-  //    bh[m][g][t] = high parts of lo[t][32 m + 8 g .. + 8] (zeros for tokens t >= T)
-  __shared__ __attribute__((aligned(16))) float lo_sm[T * R];
-  __shared__ uint4 bh[R / 32][4][16], bl[R / 32][4][16];
+  // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order.
+  //    T <= 8 (PACK): one B matrix, column t < 8 = high parts of token t, column 8 + t = its low parts:
+  //      bh[m][g][n] = parts of lo[n & 7][32 m + 8 g .. + 8]
+  //    T > 8: bh[m][g][t] and bl[m][g][t] = high and low parts of lo[t][32 m + 8 g .. + 8].
+  //    Only the T tokens' columns are staged: a column of B reaches only the same column of the
+  //    product, and the columns of tokens >= T are never stored.
+  constexpr bool PACK = T <= 8;
+  __shared__ __attribute__((aligned(16))) float lo_sm[T * R + LO_JUNK];
+  __shared__ uint4 bh[R / 32][4][16], bl[PACK ? 1 : R / 32][4][16];
   __shared__ float gate_sm[T][S];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int it = tid + n * UP_THREADS;
-    if (it < ITEMS) {
-      const int t = it / (R / 4), k = 4 * (it % (R / 4));
-      f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
-      if (INJ) vv += iv[n];
-      *reinterpret_cast<f32x4*>(lo_sm + t * R + k) = vv;
-    }
-  }
+  store_lo<T, INJ, NI, UPM_THREADS>(tid, pv, iv, lo_sm);
   __syncthreads();
-  for (int i = tid; i < (R / 32) * 4 * 16; i += UP_THREADS) {
-    const int t = i & 15, g = (i >> 4) & 3, m = i >> 6;
+  for (int i = tid; i < (R / 32) * 4 * T; i += UPM_THREADS) {
+    const int t = i % T, g = (i / T) & 3, m = i / (4 * T);
     float v8[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v8[e] = t < T ? lo_sm[t * R + 32 * m + 8 * g + e] : 0.f;
+    for (int e = 0; e < 8; ++e) v8[e] = lo_sm[t * R + 32 * m + 8 * g + e];
     uint4 hi, lo;
     split_hi_lo(v8, hi, lo);
     bh[m][g][t] = hi;
-    bl[m][g][t] = lo;
+    if constexpr (PACK)
+      bh[m][g][8 + t] = lo;
+    else
+      bl[m][g][t] = lo;
   }
   if (tid < T * S) gate_sm[tid / S][tid % S] = 1.0f / (1.0f + expf(-lo_sm[(tid / S) * R + (tid % S)]));
   if (blockIdx.x == 0)
-    for (int i = tid; i < T * R; i += UP_THREADS) lo_out[i] = lo_sm[i];
+    for (int i = tid; i < T * R; i += UPM_THREADS) lo_out[i] = lo_sm[i];
   __syncthreads();
   if (wave >= 3) return;
-  // 4. the tile on the matrix cores, K in order, high part then low part of each step
+  // 4. the tile on the matrix cores, K in order (T > 8: high part then low part of each step, into the
+  //    same accumulator; T <= 8: one product per step, then token t's high-part sum (column t) plus its
+  //    low-part sum (column 8 + t, brought over by a rotation of the 16-lane row by 8)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bh[m][lg][li]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bl[m][lg][li]), acc, 0, 0, 0);
+    if constexpr (!PACK)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bl[m][lg][li]), acc, 0, 0, 0);
+  }
+  if constexpr (PACK) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc[s] += dpp<0x128>(acc[s]);  // row_ror:8
   }
   // 5. epilogue: lane = token li, rows 16 wave + 4 lg + s = stream s of column 4 wave + lg; the stream
   //    mean in the v_dot2 kernel's order ((s0 + s1) + (s2 + s3))
@@ -642,9 +669,11 @@ static const up_fn kUp[2][TMAX][2][2] = {HCR_UP_ROW(FMT_BF16), HCR_UP_ROW(FMT_Q8
 
 #define HCR_UPM_T(T) {{hc_up_mfma<T, false, false>, hc_up_mfma<T, false, true>}, \
                       {hc_up_mfma<T, true, false>, hc_up_mfma<T, true, true>}}
-static_assert(UP_MFMA_FROM == 10 && TMAX == 16, "the table below lists T = 10..16");
-static const up_fn kUpM[TMAX - UP_MFMA_FROM + 1][2][2] = {HCR_UPM_T(10), HCR_UPM_T(11), HCR_UPM_T(12), HCR_UPM_T(13),
-                                                          HCR_UPM_T(14), HCR_UPM_T(15), HCR_UPM_T(16)};
+static_assert(TMAX == 16, "the table below lists T = 1..16");
+static const up_fn kUpM[TMAX][2][2] = {HCR_UPM_T(1),  HCR_UPM_T(2),  HCR_UPM_T(3),  HCR_UPM_T(4),
+                                       HCR_UPM_T(5),  HCR_UPM_T(6),  HCR_UPM_T(7),  HCR_UPM_T(8),
+                                       HCR_UPM_T(9),  HCR_UPM_T(10), HCR_UPM_T(11), HCR_UPM_T(12),
+                                       HCR_UPM_T(13), HCR_UPM_T(14), HCR_UPM_T(15), HCR_UPM_T(16)};
 #undef HCR_UPM_T
 
 int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, const void* w_up, const uint16_t* s_up,
@@ -658,9 +687,11 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
   hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, w_down, s_down, x, w_norm, part,
                      rs);
-  const up_fn up = fmt == FMT_BF16 && T >= UP_MFMA_FROM ? kUpM[T - UP_MFMA_FROM][inj != nullptr][pending != nullptr]
-                                                        : kUp[fmt][T - 1][inj != nullptr][pending != nullptr];
-  hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(UP_THREADS), 0, st, w_up, s_up, part, inj, pending, out, mean, lo);
+  const bool mfma = fmt == FMT_BF16 && T >= UP_MFMA_FROM;
+  const up_fn up = mfma ? kUpM[T - 1][inj != nullptr][pending != nullptr]
+                        : kUp[fmt][T - 1][inj != nullptr][pending != nullptr];
+  hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(mfma ? upm_threads(T) : UP_THREADS), 0, st, w_up, s_up, part, inj,
+                     pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }
 

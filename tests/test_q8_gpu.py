@@ -109,15 +109,18 @@ def test_q8_numerics_stress():
         check_read(s.reader, 8, out, mean, s.ref_read(c["x"][k], c["pending"][k], c["inj"][k]), f"Q8_0 stress {k}")
 
 
-def test_q8_token_results_do_not_depend_on_T(q8set):
-    T = 8
+@pytest.mark.parametrize("T", [8, 16])
+def test_q8_token_results_do_not_depend_on_T(q8set, T):
+    """Q8_0 reads (the vector-ALU up kernel at every T): each token's result is the same, bit for bit, read
+    alone or in any window of up to 16 tokens."""
     x, p, inj = gen.activations(16, T), gen.pending(16, T), gen.injection(16, T)
-    o8, m8 = q8set.reader.read(to_dev(x), to_dev(p), to_dev(inj))
-    o8, m8 = o8.clone(), m8.clone()
-    for t in range(T):
-        o1, m1 = q8set.reader.read(to_dev(x[t:t + 1]), to_dev(p[t:t + 1]), to_dev(inj[t:t + 1]))
+    of, mf = q8set.reader.read(to_dev(x), to_dev(p), to_dev(inj))
+    of, mf = of.clone(), mf.clone()
+    windows = [(t, t + 1) for t in range(T)] + ([(0, 9), (5, 16), (2, 12)] if T == 16 else [(1, 5)])
+    for a, b in windows:
+        o, m = q8set.reader.read(to_dev(x[a:b]), to_dev(p[a:b]), to_dev(inj[a:b]))
         torch.cuda.synchronize()
-        assert torch.equal(o1[0], o8[t]) and torch.equal(m1[0], m8[t]), f"token {t}"
+        assert torch.equal(o, of[a:b]) and torch.equal(m, mf[a:b]), f"tokens {a}..{b - 1}"
 
 
 @pytest.mark.parametrize("T", [1, 8, 16])
