@@ -366,8 +366,9 @@ def main():
         "config": {"workload": "cold HC read T sweep: 4 streams x 2560, R = 320, 32 rotated BF16 weight sets "
                                "(419 MB), T = 1..8, one read per set and T per step, HIP graph replay",
                    "reads_per_step": reads_per_step, "weight_sets": len(readers),
-                   "arithmetic": "bf16 weights; fp32 accumulation (down: FMA on widened weights; "
-                                 "up: v_dot2_f32_bf16 with lo split into bf16 high + low)",
+                   "arithmetic": "bf16 weights; fp32 accumulation (down: FMA on widened weights; up: "
+                                 "v_mfma_f32_16x16x32_bf16 from T = 2, v_dot2_f32_bf16 at T = 1, with lo "
+                                 "split into bf16 high + low)",
                    "per_T_us": {T: v for T, v in per_T_us.items() if T <= TMAX},
                    "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items() if T <= TMAX},
                    "wide_windows_T9_16": {"per_T_us": {T: v for T, v in per_T_us.items() if T > TMAX},
@@ -378,7 +379,8 @@ def main():
                    "verify_window": window, "q8_0": q8, "matvec_bf16": matvec},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "the read (hc_down + hc_up dispatches), event-timed per read over the timed region; "
+                     "kernel": "the read (hc_down + hc_up_mfma / hc_up dispatches), event-timed per read over the "
+                               "timed region; "
                                "traffic = counter-measured HBM bytes per read (mean over T = 1..8)"},
     }
     if not args.no_cpu_baseline:

@@ -43,7 +43,7 @@ def kernel_key(name):
     m = re.search(r"hcr::hc_up<(\d+), (true|false), (true|false), (\d+)>", name)
     if m:
         return ("up", int(m.group(1)), int(m.group(4)), m.group(2) == "true", m.group(3) == "true")
-    m = re.search(r"hcr::hc_up_mfma<(\d+), (true|false), (true|false)>", name)  # BF16, the larger windows
+    m = re.search(r"hcr::hc_up_mfma<(\d+), (true|false), (true|false)>", name)  # BF16, T >= 2 (matrix cores)
     if m:
         return ("up", int(m.group(1)), 0, m.group(2) == "true", m.group(3) == "true")
     if "hcr::q8_quantize" in name:
@@ -215,7 +215,7 @@ def main():
         rec["timed_region"].update(bench_event_us_per_read_untraced=untraced, bench_event_us_per_read_traced=traced)
         tot = tr[2] + tr[3]
         md += ["", f"Timed region of the traced bench run (its timed steps, found between two marker kernels): "
-                   f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + hc_up {tr[3]:.3f} µs = "
+                   f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + up (hc_up_mfma, hc_up at T = 1) {tr[3]:.3f} µs = "
                    f"{tot:.3f} µs per read (p10 / p50 / p90 of down + up per read: "
                    f"{tr[4][10]:.3f} / {tr[4][50]:.3f} / {tr[4][90]:.3f} µs)."
                    + (f" An untraced `python bench.py` of the same session measured {untraced:.3f} µs per read "
