@@ -16,7 +16,8 @@
 //     (halving with v_permlane32/16_swap, then DPP) and over the 8 waves (LDS,
 //     fixed order); the work-group writes rs[t][s] * (row sums), one partial
 //     per stream.
-//   hc_up_mfma<T, INJ, PEND> (BF16 weights, T >= 2): lo[t][k] = the 4 stream
+//   hc_up_mfma<T, INJ, PEND> (BF16 weights from T = 2, Q8_0 copies from T = 4):
+//     lo[t][k] = the 4 stream
 //     partials (+ injection), then 40 rows of W_up (10 columns x 4 streams) per
 //     work-group as three 16-row tiles on the matrix cores
 //     (v_mfma_f32_16x16x32_bf16), lo split into BF16 high and low parts as the
@@ -24,8 +25,8 @@
 //     parts columns 8..15, one product per K step; from 9 tokens each part has
 //     its own product.  Epilogue in the lane: pending write, sigmoid gate of
 //     lo[t][s], stream mean.
-//   hc_up<T, INJ, PEND>: the same tile on the vector ALUs (BF16 at T = 1, and
-//     every Q8_0 read).  Each row is reduced by the 32 lanes of a half-wave;
+//   hc_up<T, INJ, PEND>: the same tile on the vector ALUs (BF16 at T = 1,
+//     Q8_0 at T = 1..3).  Each row is reduced by the 32 lanes of a half-wave;
 //     lane q owns K [8q, 8q+8) and [256+2q, +2) and multiplies with
 //     v_dot2_f32_bf16 against the high and low parts of lo.  Epilogue: pending
 //     write, sigmoid gate, stream mean of 4 adjacent outputs (DPP quad).
@@ -67,15 +68,17 @@
 // the bytes of BF16) and two scales per lane and row; each of a lane's two
 // column runs sits inside one block, so the lane multiplies each run's FMA sum
 // by its block's scale.
-// The up kernel takes lo in FP32 from LDS (no BF16 split): the codes widen
-// exactly to FP32.  q8_quantize makes the copies on the device: 4 lanes per
+// The vector-ALU up kernel takes lo in FP32 from LDS (no BF16 split): the
+// codes widen exactly to FP32; the matrix-core one widens them exactly to BF16
+// and scales each block's product.  q8_quantize makes the copies on the device: 4 lanes per
 // block, the block maximum over the quad by DPP, then d = amax / 127,
 // codes = round(w * (1 / d)) with ties away from zero, all in IEEE binary32,
 // and d stored rounded to binary16.
 //
 // Determinism: every sum has a fixed order, so repeated calls and graph
 // replays are bitwise identical, and each token's result does not depend on T
-// within T = 2..8 or within T = 9..16 (BF16), or within T = 1..16 (Q8_0).
+// within T = 2..8 or within T = 9..16 (BF16), or within T = 1..3, 4..8 or
+// 9..16 (Q8_0).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -485,15 +488,32 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-// up on the matrix cores (BF16 weights, T = UP_MFMA_FROM..16).  The same work-group tile as hc_up (10
-// columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves 0..2; rows 40..47 repeat row 39
-// and are not stored) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K of W_up, B = 32 K x 16 columns
+// Q8_0 copies on the matrix cores: an MFMA K step of 32 is exactly one Q8_0 block, so the A operand is the
+// block's codes widened exactly to BF16 (|q| <= 127 needs 8 significant bits), each step's product goes to a
+// fresh accumulator, and its 4 rows are scaled by their block scales (4 FMAs per lane and step).  The WG's
+// 40 rows x 10 block scales (800 bytes) are staged in LDS as floats, sc_sm[column][block][stream].
+__device__ __forceinline__ bf16x8 codes_bf16(uint2 q) {
+  uint32_t p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t u = e < 2 ? q.x : q.y;
+    const f32x2 f = {code(u, 2 * (e & 1)), code(u, 2 * (e & 1) + 1)};
+    p[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // exact
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+}
+constexpr int SC_WORDS = S * UP_COLS * (R / Q8_BLOCK) / 2;  // 200 dwords of binary16 scales per work-group
+
+// up on the matrix cores (BF16 weights from T = UP_MFMA_FROM, Q8_0 copies from T = UP_MFMA_FROM_Q8).  The
+// same work-group tile as hc_up (10 columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves
+// 0..2; rows 40..47 repeat row 39 and are not stored) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K
+// of W_up, B = 32 K x 16 columns
 // of lo split into BF16 high and low parts.  T <= 8: column t holds token t's high parts and column
 // 8 + t its low parts (one MFMA per K step); T > 8: one B matrix of high parts and one of low parts
 // (two MFMAs per K step, high then low, into the same accumulator).  Lane (li, lg) then holds column li
 // of rows 4 lg .. 4 lg + 3 of its tile: the 4 streams of one output column, so the epilogue and the
 // stream mean stay in the lane (T <= 8: after adding column li + 8 by a row rotation).
-template <int T, bool INJ, bool PEND>
+template <int T, bool INJ, bool PEND, int FMT>
 __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
                                                   const float* __restrict__ part, const float* __restrict__ inj,
                                                   const float* pending, float* out, float* __restrict__ mean,
@@ -501,14 +521,24 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   constexpr int UPM_THREADS = upm_threads(T);
   static_assert(T <= 16 && R % 32 == 0 && UP_ROWS > 32 && UP_ROWS <= 48 && (UPM_THREADS == 192 || UPM_THREADS == 256),
                 "3 tiles of 16 rows (waves 0..2), 16 token columns");
+  static_assert(Q8_BLOCK == 32 && (R / Q8_BLOCK) % 2 == 0, "one Q8_0 block per MFMA K step; scale rows of whole dwords");
+  constexpr bool Q8 = FMT == FMT_Q8_0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = blockIdx.x * UP_COLS;
   const int li = lane & 15, lg = lane >> 4;
-  // 1. small loads first: stream partials and injection for lo, pending for the epilogue
+  // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
+  //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
   load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
+  constexpr int NSC = Q8 ? (SC_WORDS + UPM_THREADS - 1) / UPM_THREADS : 0;
+  uint32_t scw[NSC > 0 ? NSC : 1];
+#pragma unroll
+  for (int n = 0; n < NSC; ++n) {
+    const int it = min(tid + n * UPM_THREADS, SC_WORDS - 1), ss = it / (SC_WORDS / S);
+    scw[n] = reinterpret_cast<const uint32_t*>(s_up + ((size_t)ss * D + c0) * (R / Q8_BLOCK))[it % (SC_WORDS / S)];
+  }
   // epilogue lane: token li, column cc = 4 * wave + lg (valid when wave < 3, cc < 10 and li < T); the
   // pending loads are clamped to a valid (token, column), so that no branch separates the loads
   const int cc = 4 * wave + lg;
@@ -524,10 +554,16 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   //    makes the compiler wait for them before the first barrier, serialising the weight stream with the
   //    lo staging.
   const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
-  const uint16_t* row = static_cast<const uint16_t*>(w_up) + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
-  uint4 a[R / 32];
+  const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+  uint4 a[Q8 ? 1 : R / 32];   // BF16: 8 weights per step
+  uint2 qa[Q8 ? R / 32 : 1];  // Q8_0: 8 codes per step
 #pragma unroll
-  for (int m = 0; m < R / 32; ++m) a[m] = *reinterpret_cast<const uint4*>(row + 32 * m + 8 * lg);
+  for (int m = 0; m < R / 32; ++m) {
+    if constexpr (Q8)
+      qa[m] = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
+    else
+      a[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order.
@@ -540,7 +576,18 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   __shared__ __attribute__((aligned(16))) float lo_sm[T * R + LO_JUNK];
   __shared__ uint4 bh[R / 32][4][16], bl[PACK ? 1 : R / 32][4][16];
   __shared__ float gate_sm[T][S];
+  __shared__ __attribute__((aligned(16))) float sc_sm[Q8 ? 2 * SC_WORDS + 2 * 64 : 4];
   store_lo<T, INJ, NI, UPM_THREADS>(tid, pv, iv, lo_sm);
+#pragma unroll
+  for (int n = 0; n < NSC; ++n) {  // scale u of stream ss: row c0 + u / 10, block u % 10; repeats to a junk slot
+    const int it0 = tid + n * UPM_THREADS, it = min(it0, SC_WORDS - 1), ss = it / (SC_WORDS / S);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = 2 * (it % (SC_WORDS / S)) + h, col = u / (R / Q8_BLOCK), blk = u % (R / Q8_BLOCK);
+      const int at = it0 < SC_WORDS ? (col * (R / Q8_BLOCK) + blk) * S + ss : 2 * SC_WORDS + 2 * (tid & 63) + h;
+      sc_sm[at] = half_bits_to_float(scw[n] >> (16 * h));
+    }
+  }
   __syncthreads();
   for (int i = tid; i < (R / 32) * 4 * T; i += UPM_THREADS) {
     const int t = i % T, g = (i / T) & 3, m = i / (4 * T);
@@ -562,13 +609,23 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   if (wave >= 3) return;
   // 4. the tile on the matrix cores, K in order (T > 8: high part then low part of each step, into the
   //    same accumulator; T <= 8: one product per step, then token t's high-part sum (column t) plus its
-  //    low-part sum (column 8 + t, brought over by a rotation of the 16-lane row by 8)
+  //    low-part sum (column 8 + t, brought over by a rotation of the 16-lane row by 8).  Q8_0: each step
+  //    (one block) into a fresh accumulator, added times the block scales of the lane's 4 rows.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bh[m][lg][li]), acc, 0, 0, 0);
+    const bf16x8 am = Q8 ? codes_bf16(qa[m]) : __builtin_bit_cast(bf16x8, a[Q8 ? 0 : m]);
+    f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bh[m][lg][li]), Q8 ? zero : acc, 0, 0, 0);
     if constexpr (!PACK)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]), __builtin_bit_cast(bf16x8, bl[m][lg][li]), acc, 0, 0, 0);
+      pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bl[m][lg][li]), pm, 0, 0, 0);
+    if constexpr (Q8) {
+      const f32x4 dm = *reinterpret_cast<const f32x4*>(sc_sm + (min(cc, UP_COLS - 1) * (R / Q8_BLOCK) + m) * S);
+#pragma unroll
+      for (int s = 0; s < S; ++s) acc[s] = __builtin_fmaf(dm[s], pm[s], acc[s]);
+    } else {
+      acc = pm;
+    }
   }
   if constexpr (PACK) {
 #pragma unroll
@@ -591,9 +648,12 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
 
 // ---------------------------------------------------------------------------
 // Q8_0 copies on the device: 4 lanes per 32-weight block (8 BF16 weights each);
-// each lane takes Q8_CHUNKS chunks a grid-stride apart, all loads issued first
+// each lane takes Q8_CHUNKS chunks a grid-stride apart, all loads issued first (one chunk: see below)
 // ---------------------------------------------------------------------------
-constexpr int Q8_CHUNKS = 4;
+// One 16-byte chunk per lane: 1,600 work-groups per matrix of the read (~25 waves per CU).  Measured on
+// MI355X (320 x 10240, 64 rotated matrices): 4.45 us per matrix, against 4.89 / 5.30 / 5.92 us with
+// 2 / 4 / 8 chunks per lane.
+constexpr int Q8_CHUNKS = 1;
 
 __global__ __launch_bounds__(256) void q8_quantize(const uint4* __restrict__ w, size_t n_blocks,
                                                    uint2* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -667,13 +727,16 @@ static const up_fn kUp[2][TMAX][2][2] = {HCR_UP_ROW(FMT_BF16), HCR_UP_ROW(FMT_Q8
 #undef HCR_UP_ROW
 #undef HCR_UP_T
 
-#define HCR_UPM_T(T) {{hc_up_mfma<T, false, false>, hc_up_mfma<T, false, true>}, \
-                      {hc_up_mfma<T, true, false>, hc_up_mfma<T, true, true>}}
+#define HCR_UPM_T(T, F) {{hc_up_mfma<T, false, false, F>, hc_up_mfma<T, false, true, F>}, \
+                         {hc_up_mfma<T, true, false, F>, hc_up_mfma<T, true, true, F>}}
+#define HCR_UPM_ROW(F)                                                                             \
+  {HCR_UPM_T(1, F),  HCR_UPM_T(2, F),  HCR_UPM_T(3, F),  HCR_UPM_T(4, F),  HCR_UPM_T(5, F),       \
+   HCR_UPM_T(6, F),  HCR_UPM_T(7, F),  HCR_UPM_T(8, F),  HCR_UPM_T(9, F),  HCR_UPM_T(10, F),      \
+   HCR_UPM_T(11, F), HCR_UPM_T(12, F), HCR_UPM_T(13, F), HCR_UPM_T(14, F), HCR_UPM_T(15, F),      \
+   HCR_UPM_T(16, F)}
 static_assert(TMAX == 16, "the table below lists T = 1..16");
-static const up_fn kUpM[TMAX][2][2] = {HCR_UPM_T(1),  HCR_UPM_T(2),  HCR_UPM_T(3),  HCR_UPM_T(4),
-                                       HCR_UPM_T(5),  HCR_UPM_T(6),  HCR_UPM_T(7),  HCR_UPM_T(8),
-                                       HCR_UPM_T(9),  HCR_UPM_T(10), HCR_UPM_T(11), HCR_UPM_T(12),
-                                       HCR_UPM_T(13), HCR_UPM_T(14), HCR_UPM_T(15), HCR_UPM_T(16)};
+static const up_fn kUpM[2][TMAX][2][2] = {HCR_UPM_ROW(FMT_BF16), HCR_UPM_ROW(FMT_Q8_0)};
+#undef HCR_UPM_ROW
 #undef HCR_UPM_T
 
 int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, const void* w_up, const uint16_t* s_up,
@@ -687,8 +750,8 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
   hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, w_down, s_down, x, w_norm, part,
                      rs);
-  const bool mfma = fmt == FMT_BF16 && T >= UP_MFMA_FROM;
-  const up_fn up = mfma ? kUpM[T - 1][inj != nullptr][pending != nullptr]
+  const bool mfma = T >= (fmt == FMT_BF16 ? UP_MFMA_FROM : UP_MFMA_FROM_Q8);
+  const up_fn up = mfma ? kUpM[fmt][T - 1][inj != nullptr][pending != nullptr]
                         : kUp[fmt][T - 1][inj != nullptr][pending != nullptr];
   hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(mfma ? upm_threads(T) : UP_THREADS), 0, st, w_up, s_up, part, inj,
                      pending, out, mean, lo);

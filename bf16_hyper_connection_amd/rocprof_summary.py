@@ -43,9 +43,9 @@ def kernel_key(name):
     m = re.search(r"hcr::hc_up<(\d+), (true|false), (true|false), (\d+)>", name)
     if m:
         return ("up", int(m.group(1)), int(m.group(4)), m.group(2) == "true", m.group(3) == "true")
-    m = re.search(r"hcr::hc_up_mfma<(\d+), (true|false), (true|false)>", name)  # BF16, T >= 2 (matrix cores)
+    m = re.search(r"hcr::hc_up_mfma<(\d+), (true|false), (true|false), (\d+)>", name)  # matrix cores
     if m:
-        return ("up", int(m.group(1)), 0, m.group(2) == "true", m.group(3) == "true")
+        return ("up", int(m.group(1)), int(m.group(4)), m.group(2) == "true", m.group(3) == "true")
     if "hcr::q8_quantize" in name:
         return ("quantize",)
     m = re.search(r"hcr::mv_bf16<(\d+), (\d+)>", name)

@@ -24,7 +24,7 @@
  * reproducible, also as a replayed HIP graph.  A token's results are the same
  * bit for bit whatever the other tokens of the window within one range of T:
  * BF16 weights T = 2..8 and T = 9..16 (a token read alone, T = 1, rounds
- * differently), Q8_0 copies T = 1..16.
+ * differently), Q8_0 copies T = 1..3, 4..8 and 9..16.
  *
  * Memory. Every pointer is a device pointer the caller owns (the library
  * allocates nothing on the device and never frees caller memory).  Layouts

@@ -109,15 +109,20 @@ def test_q8_numerics_stress():
         check_read(s.reader, 8, out, mean, s.ref_read(c["x"][k], c["pending"][k], c["inj"][k]), f"Q8_0 stress {k}")
 
 
-@pytest.mark.parametrize("T", [8, 16])
-def test_q8_token_results_do_not_depend_on_T(q8set, T):
-    """Q8_0 reads (the vector-ALU up kernel at every T): each token's result is the same, bit for bit, read
-    alone or in any window of up to 16 tokens."""
-    x, p, inj = gen.activations(16, T), gen.pending(16, T), gen.injection(16, T)
+@pytest.mark.parametrize("lo_t,hi_t,windows", [
+    (1, 3, [(0, 1), (1, 2), (2, 3), (0, 2), (1, 3)]),
+    (4, 8, [(0, 4), (4, 8), (1, 6), (2, 8), (0, 7), (1, 8)]),
+    (9, 16, [(0, 9), (7, 16), (2, 13), (3, 15), (0, 15), (1, 16)]),
+])
+def test_q8_token_results_do_not_depend_on_T(q8set, lo_t, hi_t, windows):
+    """Q8_0 reads: within each range of T that one up kernel serves (T = 1..3 vector ALUs; T = 4..8 and
+    9..16 the matrix cores' two B layouts) each token's result is the same, bit for bit, in every window."""
+    T = hi_t
+    x, p, inj = gen.activations(16 + T, T), gen.pending(16 + T, T), gen.injection(16 + T, T)
     of, mf = q8set.reader.read(to_dev(x), to_dev(p), to_dev(inj))
     of, mf = of.clone(), mf.clone()
-    windows = [(t, t + 1) for t in range(T)] + ([(0, 9), (5, 16), (2, 12)] if T == 16 else [(1, 5)])
     for a, b in windows:
+        assert lo_t <= b - a <= hi_t
         o, m = q8set.reader.read(to_dev(x[a:b]), to_dev(p[a:b]), to_dev(inj[a:b]))
         torch.cuda.synchronize()
         assert torch.equal(o, of[a:b]) and torch.equal(m, mf[a:b]), f"tokens {a}..{b - 1}"
