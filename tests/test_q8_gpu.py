@@ -100,6 +100,18 @@ def test_q8_wide_windows(q8set, T):
     check_read(q8set.reader, T, out, mean, q8set.ref_read(x, p, inj), f"Q8_0 T={T}")
 
 
+@pytest.mark.parametrize("T", [9, 12, 16])
+@pytest.mark.parametrize("with_pending,with_inj", [(False, False), (False, True), (True, False)])
+def test_q8_wide_windows_epilogue_variants(q8set, T, with_pending, with_inj):
+    """The matrix-core kernels of the larger windows (3 waves at T = 9, 4 from T = 10) without the pending write
+    or the injection."""
+    x = gen.activations(24, T, index=T)
+    p = gen.pending(24, T, index=T) if with_pending else None
+    inj = gen.injection(24, T, index=T) if with_inj else None
+    out, mean = q8set.reader.read(to_dev(x), to_dev(p), to_dev(inj))
+    check_read(q8set.reader, T, out, mean, q8set.ref_read(x, p, inj), f"Q8_0 T={T} p={with_pending} i={with_inj}")
+
+
 def test_q8_numerics_stress():
     """Heavy-tailed x (stream RMS 1e-3..1e3), near-duplicate W_down rows, pending and inj, 4 sets, T = 8."""
     c = gen.numerics_stress(15, T=8, n_sets=4)
