@@ -117,17 +117,58 @@ def counters(d, counter):
     return {k: statistics.median(v) for k, v in vals.items()}, statistics.median(copy)
 
 
+SQ_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+               "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM"]
+
+
+def sq_table(d, commands):
+    """Markdown: per read kernel (BF16, no pending write or injection) and T, the median per dispatch of one
+    rocprofv3 --pmc pass over SQ_COUNTERS, and those counts per wave."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(_one("*counter_collection.csv", d)) as fh:
+        for r in csv.DictReader(fh):
+            k = kernel_key(r["Kernel_Name"])
+            if k and k[0] in ("down", "up") and k[2] == 0 and not k[3] and not k[4]:
+                vals[(k[0], k[1])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    md = ["# SQ counters of the read kernels (MI355X)", "", "Commands (from the repository root on the GPU box):",
+          "", "```"] + commands + ["```", "",
+          "Medians per dispatch (BF16 weights, no pending write or injection; down = `hc_down`, up = `hc_up` at "
+          "T = 1, `hc_up_mfma` from T = 2), then per wave: WAIT_ANY (waiting on anything, mostly memory), "
+          "ACTIVE_INST_VALU (the wave's VALU issue) and WAIT_INST_ANY (an instruction ready but not issued: "
+          "dependencies, or the other wave of the SIMD issuing). Counts are the counters' own units.", "",
+          "| kernel | T | waves | wave cycles | WAIT_ANY | WAIT_INST_ANY | ACTIVE_INST_ANY | ACTIVE_INST_VALU | "
+          "per wave: cycles | WAIT_ANY | VALU | WAIT_INST |",
+          "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(vals):
+        v = {n: statistics.median(vals[key][n]) for n in SQ_COUNTERS if vals[key][n]}
+        if len(v) < len(SQ_COUNTERS):
+            continue
+        w = v["SQ_WAVES"]
+        md.append(f"| {key[0]} | {key[1]} | {w:.0f} | {v['SQ_WAVE_CYCLES']:,.0f} | {v['SQ_WAIT_ANY']:,.0f} | "
+                  f"{v['SQ_WAIT_INST_ANY']:,.0f} | {v['SQ_ACTIVE_INST_ANY']:,.0f} | {v['SQ_ACTIVE_INST_VALU']:,.0f} | "
+                  f"{v['SQ_WAVE_CYCLES'] / w:.0f} | {v['SQ_WAIT_ANY'] / w:.0f} | {v['SQ_ACTIVE_INST_VALU'] / w:.0f} | "
+                  f"{v['SQ_WAIT_INST_ANY'] / w:.0f} |")
+    return "\n".join(md) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--sq", help="a rocprofv3 --pmc run over SQ_COUNTERS: write only its table to --md")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--md", required=True)
-    ap.add_argument("--json", required=True)
+    ap.add_argument("--json")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--bench-log", help="stdout of the traced bench run (its JSON line: the traced event figure)")
     ap.add_argument("--bench-json", help="the JSON line of an untraced bench.py run of the same session")
     a = ap.parse_args()
+    if a.sq:
+        with open(a.md, "w") as fh:
+            fh.write(sq_table(a.sq, a.command))
+        return
+    if not (a.trace and a.fetch and a.write and a.json):
+        ap.error("--trace, --fetch, --write and --json are required (or --sq)")
 
     dur = durations(a.trace)
     fetch, fetch_copy = counters(a.fetch, "FETCH_SIZE")
