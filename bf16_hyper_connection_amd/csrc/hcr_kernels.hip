@@ -281,7 +281,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 
 // The up kernels' first loads: the 4 stream partials (and the injection) of lo, 4 K values of one token
 // per item, items tid + n * NT (NT threads).  Neither the loads nor the stores of lo are conditional: items
-// past the end repeat the last item (the same value to the same LDS address).  A branch among the loads
+// past the end load the last item again (store_lo puts those repeats in junk slots).  A branch among the loads
 // makes the compiler wait for every load issued so far, and a branch around their only use lets it sink
 // them below the weight loads; either would serialise them with the weight stream.
 template <int T, bool INJ, int NI, int NT>
@@ -318,7 +318,8 @@ __device__ __forceinline__ void store_lo(int tid, const f32x4 (&pv)[NI][S], cons
   }
 }
 
-// up: lo = sum of the 4 stream partials (+ injection); 40 rows of W_up (10 columns x 4 streams) per work-group
+// up on the vector ALUs (BF16 at T = 1, Q8_0 at T = 1..3): lo = sum of the 4 stream partials (+ injection);
+// 40 rows of W_up (10 columns x 4 streams) per work-group
 template <int T, bool INJ, bool PEND, int FMT>
 __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_up,
                                                          const uint16_t* __restrict__ s_up,
