@@ -7,8 +7,10 @@
 // same idea becomes: a wave takes a group of 4 rows, lane l owns the 16-byte chunks
 // l, l + 64, ... of every row (one coalesced 1 KB load per chunk index), multiplies
 // them by the x values of the same columns, which the work-group stages once in LDS in
-// each lane's chunk order, and the 4 x T per-lane sums are added over the wave in one
-// multi-value reduction (v_permlane32/16_swap halving, then DPP inside rows of 16).
+// each lane's chunk order as BF16 high and low parts (v_dot2_f32_bf16 on the weights'
+// BF16 pairs as loaded: no widening; the two parts keep ~2^-17 of each x value), and the
+// 4 x T per-lane sums are added over the wave in one multi-value reduction
+// (v_permlane32/16_swap halving, then DPP inside rows of 16).
 //
 // One row group per wave, many waves per CU: on MI355X a streaming kernel reaches HBM
 // bandwidth only with many resident waves each holding a few loads in flight (measured: a
@@ -43,10 +45,11 @@ __device__ __forceinline__ void load_group(const uint4* __restrict__ w, int rows
   }
 }
 
-// FMA chains of the group's rows x T tokens (x from LDS, chunk by chunk), the wave sum, and the
-// stores of y
+// the group's rows x T tokens: per chunk, the 4 BF16 weight pairs times the x values' BF16 high parts, then
+// times their low parts (v_dot2_f32_bf16, one chain per row and token; x from LDS, chunk by chunk), the wave
+// sum, and the stores of y
 template <int T, int KCH, int XPAD>
-__device__ __forceinline__ void group_result(const uint4 (&wv)[MV_ROWS_PER_WAVE][KCH], const f32x4 (*xs)[XPAD],
+__device__ __forceinline__ void group_result(const uint4 (&wv)[MV_ROWS_PER_WAVE][KCH], const uint4 (*xs)[XPAD],
                                              int rows, int g, int lane, float* __restrict__ y) {
   constexpr int N = round4(MV_ROWS_PER_WAVE * T);  // zeros pad the values to a multiple of 4
   float v[N];
@@ -54,28 +57,25 @@ __device__ __forceinline__ void group_result(const uint4 (&wv)[MV_ROWS_PER_WAVE]
   for (int i = 0; i < N; ++i) v[i] = 0.f;
 #pragma unroll
   for (int j = 0; j < KCH; ++j) {
-    f32x4 xa[T], xb[T];
+    uint4 xh[T], xl[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      xa[t] = xs[0][(t * KCH + j) * 64 + lane];
-      xb[t] = xs[1][(t * KCH + j) * 64 + lane];
+      xh[t] = xs[0][(t * KCH + j) * 64 + lane];
+      xl[t] = xs[1][(t * KCH + j) * 64 + lane];
     }
 #pragma unroll
     for (int r = 0; r < MV_ROWS_PER_WAVE; ++r) {
       const uint32_t u[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
-      float wf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = __uint_as_float(u[e] << 16);
-        wf[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-      }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
+        const uint32_t hh[4] = {xh[t].x, xh[t].y, xh[t].z, xh[t].w};
+        const uint32_t ll[4] = {xl[t].x, xl[t].y, xl[t].z, xl[t].w};
         float acc = v[r * T + t];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(wf[e], xa[t][e], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(wf[4 + e], xb[t][e], acc);
+        for (int e = 0; e < 4; ++e) {
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u[e]), __builtin_bit_cast(bf16x2v, hh[e]), acc, false);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u[e]), __builtin_bit_cast(bf16x2v, ll[e]), acc, false);
+        }
         v[r * T + t] = acc;
       }
     }
@@ -105,13 +105,13 @@ __global__ __launch_bounds__(MV_THREADS) void mv_bf16(const uint4* __restrict__ 
   const int cols = chunks * 8;
 
   // x once per work-group into LDS, in each lane's chunk order: entry e = (t * KCH + j) * 64 + l of
-  // xs[h] holds x[t] at columns 8(l + 64 j) + 4h .. +4 (zeros past the row), so lane l of every wave
-  // reads 16 consecutive bytes.  A thread issues its x loads first, then the wave's weight loads,
+  // xs[0] (xs[1]) holds the BF16 high (low) parts of x[t] at columns 8(l + 64 j) .. +8 (zeros past the
+  // row), so lane l of every wave reads 16 consecutive bytes.  A thread issues its x loads first, then the wave's weight loads,
   // and writes LDS once the x loads (the older ones) are back; the LDS array is padded to whole
   // passes of the work-group so that no write needs a branch.
   constexpr int XS = T * KCH * 64;
   constexpr int XIT = (XS + MV_THREADS - 1) / MV_THREADS;
-  __shared__ f32x4 xs[2][XIT * MV_THREADS];
+  __shared__ uint4 xs[2][XIT * MV_THREADS];  // BF16 high parts, low parts
   f32x4 xl[XIT][2];
   bool xin[XIT];
 #pragma unroll
@@ -137,8 +137,16 @@ __global__ __launch_bounds__(MV_THREADS) void mv_bf16(const uint4* __restrict__ 
 #pragma unroll
   for (int it = 0; it < XIT; ++it) {
     const float keep = xin[it] ? 1.f : 0.f;
-    xs[0][threadIdx.x + it * MV_THREADS] = xl[it][0] * keep;
-    xs[1][threadIdx.x + it * MV_THREADS] = xl[it][1] * keep;
+    float v8[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v8[e] = xl[it][0][e] * keep;
+      v8[4 + e] = xl[it][1][e] * keep;
+    }
+    uint4 hi, lo;
+    split_hi_lo(v8, hi, lo);
+    xs[0][threadIdx.x + it * MV_THREADS] = hi;
+    xs[1][threadIdx.x + it * MV_THREADS] = lo;
   }
   __syncthreads();
 
