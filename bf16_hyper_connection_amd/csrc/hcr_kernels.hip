@@ -258,25 +258,24 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
   // 4. sums over the wave, then over the waves in a fixed order
   wave_sum<N>(v);
   __shared__ float wsum[DOWN_WAVES][N];
-  __shared__ float tot[N];
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) wsum[wave][(lane >> 4) * (N / 4) + i] = v[i];
   }
   __syncthreads();
-  if (tid < N) {
-    float a = wsum[0][tid];
-#pragma unroll
-    for (int k = 1; k < DOWN_WAVES; ++k) a += wsum[k][tid];
-    tot[tid] = a;
-  }
-  __syncthreads();
 
-  // 5. rs of this stream per token, and the rs-scaled partial sums of the 5 rows
+  // 5. rs of this stream per token, and the rs-scaled partial sums of the 5 rows: thread (r, t) adds its
+  //    value and its token's sum of squares over the waves itself (no second barrier)
   if (tid < DOWN_ROWS * T) {
     const int r = tid / T, t = tid % T;
-    const float rs = 1.0f / __builtin_sqrtf(tot[DOWN_ROWS * T + t] * (1.0f / D) + 1e-6f);
-    part[((size_t)s * TMAX + t) * R + DOWN_ROWS * g + r] = rs * tot[r * T + t];
+    float a = wsum[0][r * T + t], q = wsum[0][DOWN_ROWS * T + t];
+#pragma unroll
+    for (int k = 1; k < DOWN_WAVES; ++k) {
+      a += wsum[k][r * T + t];
+      q += wsum[k][DOWN_ROWS * T + t];
+    }
+    const float rs = 1.0f / __builtin_sqrtf(q * (1.0f / D) + 1e-6f);
+    part[((size_t)s * TMAX + t) * R + DOWN_ROWS * g + r] = rs * a;
     if (g == 0 && r == 0) rs_out[t * S + s] = rs;
   }
 }
