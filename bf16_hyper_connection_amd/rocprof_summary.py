@@ -130,8 +130,9 @@ def sq_table(d, commands):
             k = kernel_key(r["Kernel_Name"])
             if k and k[0] in ("down", "up") and k[2] == 0 and not k[3] and not k[4]:
                 vals[(k[0], k[1])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    from bf16_hyper_connection_amd.build import source_hash
     md = ["# SQ counters of the read kernels (MI355X)", "", "Commands (from the repository root on the GPU box):",
-          "", "```"] + commands + ["```", "",
+          "", "```"] + commands + ["```", "", f"Library sources sha256 {source_hash()[:16]}…", "",
           "Medians per dispatch (BF16 weights, no pending write or injection; down = `hc_down`, up = `hc_up` at "
           "T = 1, `hc_up_mfma` from T = 2), then per wave: WAIT_ANY (waiting on anything, mostly memory), "
           "ACTIVE_INST_VALU (the wave's VALU issue) and WAIT_INST_ANY (an instruction ready but not issued: "
