@@ -217,7 +217,10 @@ class HCRead:
             self.handle = None
 
     def read(self, x, pending=None, inj=None, out=None, mean=None, stream=None):
-        """Enqueue one read of T = x.shape[0] tokens; returns (out, mean)."""
+        """Enqueue one read of T = x.shape[0] tokens on torch's current stream (or on ``stream``, a raw
+        hipStream_t); returns (out, mean).  out and mean allocated here belong to torch's current stream:
+        with another ``stream``, pass them in (or record them on that stream) so that torch does not reuse
+        their memory before the read has run."""
         S, d, R = self.geometry
         T = x.shape[0]
         if out is None:
