@@ -209,8 +209,10 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
       load_x(grp + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // 3. per row: the weights widened exactly to FP32, one FMA chain per token
-    //    (Q8_0: one chain per block chunk, each times its block's scale)
+    // 3. per row: the weights widened exactly to FP32, one FMA chain per token.  Q8_0: below 4 tokens one
+    //    chain per block chunk, each times its block's scale; from 4 tokens the codes are first decoded to
+    //    d * q (exact in FP32: 11 + 7 significant bits), once per row, and then take the BF16 path's chain
+    constexpr bool DECODE = FMT == FMT_Q8_0 && T >= 4;
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
       float wv[NC];
@@ -231,12 +233,19 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
         for (int e = 0; e < CA; ++e) wv[e] = code(wa[r][e / 4], e % 4);
 #pragma unroll
         for (int e = 0; e < CB; ++e) wv[CA + e] = code(wb[r], e);
+        if constexpr (DECODE) {
+          const float da = half_bits_to_float(sa[r]), db = half_bits_to_float(sb[r]);
+#pragma unroll
+          for (int e = 0; e < CA; ++e) wv[e] *= da;
+#pragma unroll
+          for (int e = 0; e < CB; ++e) wv[CA + e] *= db;
+        }
       }
 #pragma unroll
       for (int i = 0; i < TG; ++i) {
         const int t = grp * TG + i;
         if (t < T) {
-          if constexpr (FMT == FMT_BF16) {
+          if constexpr (FMT == FMT_BF16 || DECODE) {
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < NC; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
