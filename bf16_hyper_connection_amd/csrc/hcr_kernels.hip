@@ -67,7 +67,8 @@
 // The same two kernels, templated on the weight format, read int8 codes (half
 // the bytes of BF16) and two scales per lane and row; each of a lane's two
 // column runs sits inside one block, so the lane multiplies each run's FMA sum
-// by its block's scale.
+// by its block's scale (the down kernel from 4 tokens: the codes times their
+// scale first, exact in FP32, once per row).
 // The vector-ALU up kernel takes lo in FP32 from LDS (no BF16 split): the
 // codes widen exactly to FP32; the matrix-core one widens them exactly to BF16
 // and scales each block's product.  q8_quantize makes the copies on the device: 4 lanes per
