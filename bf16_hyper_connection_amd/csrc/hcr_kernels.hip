@@ -159,7 +159,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
       if constexpr (CB == 2)
         wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
       else
-        wb[r] = (uint32_t)wr[(size_t)r * DD + cb] << 16;  // the weight in the high half (its FP32 position)
+        wb[r] = wr[(size_t)r * DD + cb];  // widened at its use: a shift here would wait for the load
     }
   } else {
     const int8_t* wr = static_cast<const int8_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
@@ -206,10 +206,11 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
         v[DOWN_ROWS * T + t] = ss;
       }
     }
-    if (grp + 1 < NG) {  // the next group's x streams in while this group computes
-      load_x(grp + 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // the next group's x streams in while this group computes.  The activations and sums of squares need
+    // only x and w_norm: kept ahead of every use of the weights, so that they run while the weight loads are
+    // in flight (the compiler would otherwise widen the 2-byte weight loads first, and so wait for them)
+    if (grp + 1 < NG) load_x(grp + 1);
+    __builtin_amdgcn_sched_barrier(0);
     // 3. per row: the weights widened exactly to FP32, one FMA chain per token.  Q8_0: below 4 tokens one
     //    chain per block chunk, each times its block's scale; from 4 tokens the codes are first decoded to
     //    d * q (exact in FP32: 11 + 7 significant bits), once per row, and then take the BF16 path's chain
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
           wv[CA] = __uint_as_float(wb[r] << 16);
           wv[CA + 1] = __uint_as_float(wb[r] & 0xffff0000u);
         } else {
-          wv[CA] = __uint_as_float(wb[r]);
+          wv[CA] = __uint_as_float(wb[r] << 16);
         }
       } else {
 #pragma unroll
