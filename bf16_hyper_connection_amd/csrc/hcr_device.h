@@ -54,27 +54,37 @@ __device__ __forceinline__ float dpp(float v) {
 // halving steps (v_permlane32_swap, v_permlane16_swap) then a butterfly inside
 // each row of 16 lanes; afterwards every lane l holds, in v[0 .. N/4), the
 // totals of values (l >> 4) * N/4 + i.  The order of the additions is fixed.
+//
+// The steps of value i touch only the quadruple of positions i mod N/4 + {0, 1, 2, 3} * N/4, and every value
+// meets the same lane pairings (l ^ 32, l ^ 16, then the butterfly), so its total does not depend on its
+// position: wave_quad_sum reduces one quadruple, and a caller may reduce the quadruples in any order (for
+// instance each as soon as its four values are known) with the same results as wave_sum.
 template <int N>
-__device__ __forceinline__ void wave_sum(float (&v)[N]) {
+__device__ __forceinline__ void wave_quad_sum(float (&v)[N], int q) {
   static_assert(N % 4 == 0, "wave_sum needs a multiple of 4 values");
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
+  for (int h = 0; h < 2; ++h) {
+    const int i = q + h * (N / 4);
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 2]), false, false);
     v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // lanes < 32: value i; lanes >= 32: value i + N/2
   }
-#pragma unroll
-  for (int i = 0; i < N / 4; ++i) {
-    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + N / 4]), false, false);
-    v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // even rows: value i; odd rows: value i + N/4
-  }
-#pragma unroll
-  for (int i = 0; i < N / 4; ++i) {
-    v[i] += dpp<0xB1>(v[i]);   // quad_perm [1,0,3,2]
-    v[i] += dpp<0x4E>(v[i]);   // quad_perm [2,3,0,1]
-    v[i] += dpp<0x141>(v[i]);  // row_half_mirror
-    v[i] += dpp<0x140>(v[i]);  // row_mirror
-  }
+  const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[q]), __float_as_uint(v[q + N / 4]), false, false);
+  v[q] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);  // even rows: value q; odd rows: value q + N/4
+  v[q] += dpp<0xB1>(v[q]);   // quad_perm [1,0,3,2]
+  v[q] += dpp<0x4E>(v[q]);   // quad_perm [2,3,0,1]
+  v[q] += dpp<0x141>(v[q]);  // row_half_mirror
+  v[q] += dpp<0x140>(v[q]);  // row_mirror
 }
+
+template <int N>
+__device__ __forceinline__ void wave_sum(float (&v)[N]) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) wave_quad_sum<N>(v, q);
+}
+
+// Position in a wave_sum array of N values of the k-th value in the order the values become known: the
+// k-th value goes to quadruple k / 4, so that values known early complete their quadruples early.
+constexpr int quad_pos(int k, int n) { return k / 4 + (k % 4) * (n / 4); }
 
 constexpr int round4(int n) { return (n + 3) & ~3; }
 

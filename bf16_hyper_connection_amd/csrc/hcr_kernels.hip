@@ -13,9 +13,9 @@
 //     the lane computes x*w_norm and the sums of squares of its columns for
 //     the T tokens, and one FP32 FMA chain per (row, token) over the exactly
 //     widened BF16 weights.  The 6T per-lane values are summed over the wave
-//     (halving with v_permlane32/16_swap, then DPP) and over the 8 waves (LDS,
-//     fixed order); the work-group writes rs[t][s] * (row sums), one partial
-//     per stream.
+//     (halving with v_permlane32/16_swap, then DPP; each group of four values
+//     as soon as its row is done) and over the 8 waves (LDS, fixed order); the
+//     work-group writes rs[t][s] * (row sums), one partial per stream.
 //   hc_up_mfma<T, INJ, PEND> (BF16 weights from T = 2, Q8_0 copies from T = 4):
 //     lo[t][k] = the 4 stream
 //     partials (+ injection), then 40 rows of W_up (10 columns x 4 streams) per
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
         wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
       else
         wb[r] = wr[(size_t)r * DD + cb];  // widened at its use: a shift here would wait for the load
+      __builtin_amdgcn_sched_barrier(0);  // rows in order: row r's loads complete before row r + 1's
     }
   } else {
     const int8_t* wr = static_cast<const int8_t*>(w_down) + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
@@ -178,14 +179,22 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
         wb[r] = *reinterpret_cast<const uint8_t*>(wr + (size_t)r * DD + cb);
       sa[r] = sr[(size_t)r * (DD / Q8_BLOCK) + ca / Q8_BLOCK];
       sb[r] = sr[(size_t)r * (DD / Q8_BLOCK) + cb / Q8_BLOCK];
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // The lane's 6T values, in the order they become known: the T sums of squares (value t), then the rows
+  // (value (r + 1) T + t), then padding; value k sits at quad_pos(k, N), so that the wave reduction of each
+  // quadruple can start as soon as its four values are known (with one token group: the sums of squares
+  // under the weight loads, each row's quadruples while the next rows' weights arrive)
   constexpr int N = round4((DOWN_ROWS + 1) * T);
+  constexpr bool EARLY = NG == 1;
+  // quadruples whose values are all known once the sums of squares (c = 0) and rows 0 .. c - 1 are
+  constexpr auto quads_known = [](int c) { return c >= DOWN_ROWS ? N / 4 : ((c + 1) * T) / 4; };
   float v[N];
 #pragma unroll
-  for (int i = (DOWN_ROWS + 1) * T; i < N; ++i) v[i] = 0.f;
+  for (int k = (DOWN_ROWS + 1) * T; k < N; ++k) v[quad_pos(k, N)] = 0.f;
 #pragma unroll
   for (int grp = 0; grp < NG; ++grp) {
     // 2. activations x*w_norm (unscaled) and the lane's sums of squares of this group's tokens
@@ -203,8 +212,12 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
         for (int e = 0; e < CA; ++e) ss = __builtin_fmaf(xv[i].a[e], xv[i].a[e], ss);
 #pragma unroll
         for (int e = 0; e < CB; ++e) ss = __builtin_fmaf(xv[i].b[e], xv[i].b[e], ss);
-        v[DOWN_ROWS * T + t] = ss;
+        v[quad_pos(t, N)] = ss;
       }
+    }
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int q = 0; q < quads_known(0); ++q) wave_quad_sum<N>(v, q);
     }
     // the next group's x streams in while this group computes.  The activations and sums of squares need
     // only x and w_norm: kept ahead of every use of the weights, so that they run while the weight loads are
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < NC; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
-            v[r * T + t] = acc;
+            v[quad_pos((r + 1) * T + t, N)] = acc;
           } else {
             float a8 = 0.f;
 #pragma unroll
@@ -259,15 +272,19 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
             float a2 = wv[CA] * act[i][CA];
 #pragma unroll
             for (int e = 1; e < CB; ++e) a2 = __builtin_fmaf(wv[CA + e], act[i][CA + e], a2);
-            v[r * T + t] = __builtin_fmaf(half_bits_to_float(sa[r]), a8, half_bits_to_float(sb[r]) * a2);
+            v[quad_pos((r + 1) * T + t, N)] = __builtin_fmaf(half_bits_to_float(sa[r]), a8, half_bits_to_float(sb[r]) * a2);
           }
         }
+      }
+      if constexpr (EARLY) {  // 4. sums over the wave of the quadruples this row completes
+#pragma unroll
+        for (int q = quads_known(r); q < quads_known(r + 1); ++q) wave_quad_sum<N>(v, q);
       }
     }
   }
 
-  // 4. sums over the wave, then over the waves in a fixed order
-  wave_sum<N>(v);
+  // 4. sums over the wave (several token groups: all at the end), then over the waves in a fixed order
+  if constexpr (!EARLY) wave_sum<N>(v);
   __shared__ float wsum[DOWN_WAVES][N];
   if ((lane & 15) == 0) {
 #pragma unroll
@@ -279,11 +296,12 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
   //    value and its token's sum of squares over the waves itself (no second barrier)
   if (tid < DOWN_ROWS * T) {
     const int r = tid / T, t = tid % T;
-    float a = wsum[0][r * T + t], q = wsum[0][DOWN_ROWS * T + t];
+    const int pr = quad_pos((r + 1) * T + t, N), pq = quad_pos(t, N);
+    float a = wsum[0][pr], q = wsum[0][pq];
 #pragma unroll
     for (int k = 1; k < DOWN_WAVES; ++k) {
-      a += wsum[k][r * T + t];
-      q += wsum[k][DOWN_ROWS * T + t];
+      a += wsum[k][pr];
+      q += wsum[k][pq];
     }
     const float rs = 1.0f / __builtin_sqrtf(q * (1.0f / D) + 1e-6f);
     part[((size_t)s * TMAX + t) * R + DOWN_ROWS * g + r] = rs * a;
