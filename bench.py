@@ -195,6 +195,30 @@ def main():
         log(f"bench: cold check T={T}: {row}")
     del extra
 
+    # the full epilogue (pending write and injection on) over the same 32 rotated weight sets: T = 4 with the
+    # seeded x, pending and injection of the full-epilogue workload, and T = 8 with those of the numerics-stress
+    # workload (heavy-tailed x); the weight values do not change the time of a read
+    full_epilogue = {}
+    for T, seed, xgen in ((4, 7, gen.activations), (TMAX, 5, gen.heavy_tailed_activations)):
+        ex = [torch.from_numpy(xgen(seed, T, index=k)).to(dev) for k in range(len(readers))]
+        ep = [torch.from_numpy(gen.pending(seed, T, index=k)).to(dev) for k in range(len(readers))]
+        ei = [torch.from_numpy(gen.injection(seed, T, index=k)).to(dev) for k in range(len(readers))]
+        ge = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(ge, stream=stream):
+                for k, r in enumerate(readers):
+                    r.read(ex[k], ep[k], ei[k], out=outs[T], mean=means[T])
+        torch.cuda.current_stream().wait_stream(stream)
+        us = timed(ge, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers))
+        full_epilogue[T] = {"us_per_read": round(us, 3),
+                            "algorithmic_GBps": round(algorithmic_bytes(T, pending=True, inj=True) / us / 1e3, 1)}
+        log(f"bench: full epilogue T={T} {us:.3f} us/read")
+        del ge, ex, ep, ei
+    full_epilogue["note"] = ("pending write and injection on, 32 rotated weight sets; T = 4: the full-epilogue "
+                             "inputs (seed 7), T = 8: the numerics-stress inputs (seed 5); not part of the "
+                             "timed step")
+
     # the timed steps: the whole sweep per step
     g = capture(range(1, TMAX + 1), len(readers))
     reads_per_step = TMAX * len(readers)
@@ -375,7 +399,7 @@ def main():
                                           "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items()
                                                                      if T > TMAX},
                                           "note": "same cold rotation, not part of the timed step"},
-                   "cold_cache_check_us_per_read": cold_check,
+                   "cold_cache_check_us_per_read": cold_check, "full_epilogue": full_epilogue,
                    "verify_window": window, "q8_0": q8, "matvec_bf16": matvec},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
