@@ -115,9 +115,10 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
                                                            const float* __restrict__ x,
                                                            const float* __restrict__ w_norm,
                                                            float* __restrict__ part, float* __restrict__ rs_out) {
-  // consecutive work-groups take consecutive streams: the XCD of work-group b (b mod 8) sees one stream
-  const int s = blockIdx.x & (S - 1);
-  const int g = blockIdx.x >> 2;  // rows DOWN_ROWS*g ..
+  // consecutive work-groups take consecutive streams: the XCD of work-group b (b mod 8) sees one stream, and
+  // half of its row groups, contiguous
+  const int s = down_stream(blockIdx.x);
+  const int g = down_group(blockIdx.x);  // rows DOWN_ROWS*g ..
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int CA = DOWN_CA, CB = DOWN_CB, NC = CA + CB;
   const int ca = (2048 / DOWN_WAVES) * wave + CA * lane;        // CA columns: one 2*CA-byte chunk per row
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
                                                          float* __restrict__ lo_out) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, q = lane & 31;  // half-wave (row of the iteration), K lane
-  const int c0 = blockIdx.x * UP_COLS;
+  const int c0 = up_tile(blockIdx.x) * UP_COLS;  // an XCD's tiles are contiguous
 
   // 1. small loads first (vector loads complete in issue order): stream partials and injection
   //    for lo, pending for the epilogue
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   static_assert(Q8_BLOCK == 32 && (R / Q8_BLOCK) % 2 == 0, "one Q8_0 block per MFMA K step; scale rows of whole dwords");
   constexpr bool Q8 = FMT == FMT_Q8_0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c0 = blockIdx.x * UP_COLS;
+  const int c0 = up_tile(blockIdx.x) * UP_COLS;  // an XCD's tiles are contiguous
   const int li = lane & 15, lg = lane >> 4;
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
   //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes

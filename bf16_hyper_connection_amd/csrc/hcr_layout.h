@@ -16,10 +16,18 @@ constexpr int R = HCR_RANK;        // down rows = up K
 constexpr int TMAX = HCR_T_MAX;    // tokens per read
 constexpr int DD = S * D;          // 10240: down K = up rows
 
+// ---- work-group b runs on XCD b mod XCDS (each XCD has its own L2): the tiles of one XCD are kept
+// contiguous, so that the 128-byte lines the work-groups share (rows of partials; pending, out and mean)
+// stay in one L2
+constexpr int XCDS = 8;
 // ---- down kernel: one work-group = one stream (2,560 columns) x 5 rows of W_down; 8 waves (two
 // per SIMD), lane l of wave w owns stream columns [256w + 4l, +4) and 2048 + 64w + l
 constexpr int DOWN_ROWS = 5;
 constexpr int DOWN_WGS = S * (R / DOWN_ROWS);  // 256
+// down work-group b: stream b mod 4 (XCDs k and k + 4 serve stream k), row group g; XCD k takes row groups
+// 0 .. 31 of its stream and XCD k + 4 row groups 32 .. 63
+constexpr int down_stream(int b) { return b % S; }
+constexpr int down_group(int b) { return ((b % XCDS) / S) * (DOWN_WGS / XCDS) + b / XCDS; }
 constexpr int DOWN_WAVES = 8;
 constexpr int DOWN_THREADS = 64 * DOWN_WAVES;
 constexpr int DOWN_CA = 32 / DOWN_WAVES, DOWN_CB = 8 / DOWN_WAVES;  // a lane's columns per row: CA at ca, CB at cb
@@ -29,6 +37,8 @@ static_assert((DOWN_WAVES == 4 || DOWN_WAVES == 8) && DOWN_CA * 64 * DOWN_WAVES 
 // a row is reduced by the 32 lanes of a half-wave, lane q owning K [8q, 8q+8) and [256 + 2q, +2)
 constexpr int UP_COLS = 10;
 constexpr int UP_WGS = D / UP_COLS;                          // 256
+// column tile of up work-group b: XCD k = b mod 8 takes tiles 32k .. 32k + 31
+constexpr int up_tile(int b) { return (b % XCDS) * (UP_WGS / XCDS) + b / XCDS; }
 constexpr int UP_THREADS = 256;
 constexpr int UP_ROWS = UP_COLS * S;                         // 40
 constexpr int UP_WAVE_ROWS = UP_ROWS / (UP_THREADS / 64);    // 10
@@ -47,6 +57,8 @@ constexpr size_t OFF_RS = align256(OFF_LO + size_t(TMAX) * R * 4);             /
 constexpr size_t SCRATCH_BYTES = align256(OFF_RS + size_t(TMAX) * S * 4);
 
 static_assert(S == 4 && D == 4 * 512 + 4 * 128 && R % DOWN_ROWS == 0, "down tiling must divide the geometry");
+static_assert(XCDS % S == 0 && DOWN_WGS % XCDS == 0 && UP_WGS % XCDS == 0 && XCDS * (DOWN_WGS / XCDS) == DOWN_WGS,
+              "work-groups spread evenly over the XCDs");
 static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0, "up tiling must divide the geometry");
 
 // ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
