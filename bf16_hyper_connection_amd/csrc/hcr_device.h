@@ -85,6 +85,18 @@ __device__ __forceinline__ void wave_sum(float (&v)[N]) {
 // Position in a wave_sum array of N values of the k-th value in the order the values become known: the
 // k-th value goes to quadruple k / 4, so that values known early complete their quadruples early.
 constexpr int quad_pos(int k, int n) { return k / 4 + (k % 4) * (n / 4); }
+constexpr bool quad_pos_ok() {  // a permutation of 0 .. n - 1 that puts value k in quadruple k / 4
+  for (int n = 4; n <= 128; n += 4) {
+    bool seen[128] = {};
+    for (int k = 0; k < n; ++k) {
+      const int p = quad_pos(k, n);
+      if (p < 0 || p >= n || seen[p] || p % (n / 4) != k / 4) return false;
+      seen[p] = true;
+    }
+  }
+  return true;
+}
+static_assert(quad_pos_ok(), "quad_pos must permute the positions by quadruple");
 
 constexpr int round4(int n) { return (n + 3) & ~3; }
 

@@ -59,6 +59,27 @@ constexpr size_t SCRATCH_BYTES = align256(OFF_RS + size_t(TMAX) * S * 4);
 static_assert(S == 4 && D == 4 * 512 + 4 * 128 && R % DOWN_ROWS == 0, "down tiling must divide the geometry");
 static_assert(XCDS % S == 0 && DOWN_WGS % XCDS == 0 && UP_WGS % XCDS == 0 && XCDS * (DOWN_WGS / XCDS) == DOWN_WGS,
               "work-groups spread evenly over the XCDs");
+
+// the work-group maps, checked at compile time: each tile once, and the tiles of one XCD contiguous
+constexpr bool up_tiles_ok() {
+  bool seen[UP_WGS] = {};
+  for (int b = 0; b < UP_WGS; ++b) {
+    const int t = up_tile(b), k = b % XCDS;
+    if (t < 0 || t >= UP_WGS || seen[t] || t / (UP_WGS / XCDS) != k) return false;
+    seen[t] = true;
+  }
+  return true;
+}
+constexpr bool down_groups_ok() {
+  bool seen[S][R / DOWN_ROWS] = {};
+  for (int b = 0; b < DOWN_WGS; ++b) {
+    const int s = down_stream(b), g = down_group(b), k = b % XCDS;
+    if (s != k % S || g < 0 || g >= R / DOWN_ROWS || seen[s][g] || g / (DOWN_WGS / XCDS) != k / S) return false;
+    seen[s][g] = true;
+  }
+  return true;
+}
+static_assert(up_tiles_ok() && down_groups_ok(), "the work-group maps must cover every tile once, per XCD contiguous");
 static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0, "up tiling must divide the geometry");
 
 // ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
