@@ -35,11 +35,11 @@ template <int KCH>
 __device__ __forceinline__ void load_group(const uint4* __restrict__ w, int rows, int chunks, int g, int lane,
                                            uint4 (&wv)[MV_ROWS_PER_WAVE][KCH]) {
 #pragma unroll
-  for (int r = 0; r < MV_ROWS_PER_WAVE; ++r) {
-    const int row = min(g * MV_ROWS_PER_WAVE + r, rows - 1);
+  for (int j = 0; j < KCH; ++j) {  // chunk by chunk, the order the products use them
+    const int c = min(lane + 64 * j, chunks - 1);
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = min(lane + 64 * j, chunks - 1);
+    for (int r = 0; r < MV_ROWS_PER_WAVE; ++r) {
+      const int row = min(g * MV_ROWS_PER_WAVE + r, rows - 1);
       wv[r][j] = w[(size_t)row * chunks + c];
     }
   }
