@@ -59,7 +59,14 @@
 //
 // Loads: vector-memory loads complete in issue order, so every kernel issues
 // its small inputs first (x, w_norm; partials, injection, pending) and its
-// weight tile after them, all before any arithmetic.
+// weight tile after them, all before any arithmetic; the weights go in the
+// order the arithmetic uses them (row by row in hc_down, K step by K step in
+// hc_up_mfma), and arithmetic that needs only the small inputs is kept ahead
+// of every use of the weights, so that it runs while they are in flight.
+//
+// Work-group b runs on XCD b mod 8, each XCD with its own L2: the tiles of one
+// XCD are contiguous (up_tile, down_group), so that the 128-byte lines that
+// neighbouring tiles share (partials; pending, out and mean) stay in one L2.
 //
 // Q8_0 copies (Strata PR #2812, Summary: the sibling read of #2810 on Q8_0
 // copies of the projections; the block is read as GGML's Q8_0: 32 weights of
