@@ -62,6 +62,20 @@ def measured_traffic(fmt="bf16"):
     return d.get(fmt, {}).get("bytes_per_read_mean_T1_8")
 
 
+def measured_matvec_traffic():
+    """HBM bytes per matvec call (mean over T = 1..4) from the same counter summary, or None."""
+    from bf16_hyper_connection_amd import build
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    mv = d.get("matvec_bf16")
+    if d.get("source_sha256") != build.source_hash() or not mv:
+        return None
+    return round(sum(v["hbm_bytes"] for v in mv.values()) / len(mv))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -326,7 +340,7 @@ def main():
                   "roofline": {"bound": "hbm", "achieved": round(sum(mv_T_gbps.values()) / len(mv_T_gbps), 1),
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "frac": round(sum(mv_T_gbps.values()) / len(mv_T_gbps) / HBM_PEAK_GBPS, 4),
-                               "best_frac": round(best / HBM_PEAK_GBPS, 4)},
+                               "best_frac": round(best / HBM_PEAK_GBPS, 4), "traffic": measured_matvec_traffic()},
                   "note": "y = W x, BF16 weights, 1..4 columns; graphs of 8 calls over the rotated copies; "
                           "not part of the timed step"}
         del mw
