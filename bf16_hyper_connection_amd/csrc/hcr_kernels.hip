@@ -44,8 +44,8 @@
 // 7.03 us (v_dot2) against 7.21 (matrix cores), T = 2 7.60 against 7.56,
 // T = 8 10.42 against 9.28.
 //
-// T = 14..16: the down kernel takes the tokens in groups of 8 (the next
-// group's x loads overlap the current group's FMAs); up to 13 in one group.  A token's result is the
+// T = 10..16: the down kernel takes the tokens in groups of 8 (the next
+// group's x loads overlap the current group's FMAs); up to 9 in one group.  A token's result is the
 // same bit for bit at every T of one range: T = 2..8 and T = 9..16 (the two
 // B layouts round differently); a token read alone (T = 1, v_dot2) rounds
 // differently again.
@@ -131,11 +131,11 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
   const int ca = (2048 / DOWN_WAVES) * wave + CA * lane;        // CA columns: one 2*CA-byte chunk per row
   const int cb = 2048 + (512 / DOWN_WAVES) * wave + CB * lane;  // CB columns
 
-  // Up to 13 tokens are taken in one group (every x load issued up front, <= 160 VGPRs); from 14 tokens in
-  // groups of 8 (x of one group in registers at a time, the next group's loads under this group's FMAs).
-  // Measured on MI355X (whole read, BF16): one group is 0.1-0.3 us faster at T = 9..13 and 0.1 us slower at
-  // T = 14..16.
-  constexpr int TG = T <= 13 ? T : 8;
+  // Up to 9 tokens are taken in one group (every x load issued up front); from 10 tokens in groups of 8 (x of
+  // one group in registers at a time, the next group's loads under this group's FMAs).  Measured on MI355X
+  // (whole read, one process, alternating): groups of 8 are 0.08 / 0.04 / 0 / 0.22 us faster than one group
+  // at T = 10 / 11 / 12 / 13 for BF16 weights, and up to 0.15 us for the Q8_0 copies.
+  constexpr int TG = T <= 9 ? T : 8;
   constexpr int NG = (T + TG - 1) / TG;
   Cols<CA, CB> xv[TG];
   auto load_x = [&](int grp) {
