@@ -41,6 +41,23 @@ __device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// Weight loads: every weight is read once per call, so the loads are non-temporal (the nt bit).  Measured on
+// MI355X (cold BF16 read, one process, alternating with ordinary loads): 0.26 us faster per read on the mean
+// over T = 1..8, 0.42 us at T = 1.
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+__device__ __forceinline__ uint4 ldw16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ldw8(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ldw4(const void* p) { return __builtin_nontemporal_load(static_cast<const uint32_t*>(p)); }
+__device__ __forceinline__ uint32_t ldw2(const void* p) { return __builtin_nontemporal_load(static_cast<const uint16_t*>(p)); }
+__device__ __forceinline__ uint32_t ldw1(const void* p) { return __builtin_nontemporal_load(static_cast<const uint8_t*>(p)); }
+
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 
 __device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }

@@ -158,16 +158,16 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
       if constexpr (CA == 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(wr + (size_t)r * DD + ca);
+        const uint4 v = ldw16(wr + (size_t)r * DD + ca);
         wa[r][0] = v.x, wa[r][1] = v.y, wa[r][2] = v.z, wa[r][3] = v.w;
       } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
+        const uint2 v = ldw8(wr + (size_t)r * DD + ca);
         wa[r][0] = v.x, wa[r][1] = v.y;
       }
       if constexpr (CB == 2)
-        wb[r] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + cb);
+        wb[r] = ldw4(wr + (size_t)r * DD + cb);
       else
-        wb[r] = wr[(size_t)r * DD + cb];  // widened at its use: a shift here would wait for the load
+        wb[r] = ldw2(wr + (size_t)r * DD + cb);  // widened at its use: a shift here would wait for the load
       __builtin_amdgcn_sched_barrier(0);  // rows in order: row r's loads complete before row r + 1's
     }
   } else {
@@ -176,17 +176,17 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 #pragma unroll
     for (int r = 0; r < DOWN_ROWS; ++r) {
       if constexpr (CA == 8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(wr + (size_t)r * DD + ca);
+        const uint2 v = ldw8(wr + (size_t)r * DD + ca);
         wa[r][0] = v.x, wa[r][1] = v.y;
       } else {
-        wa[r][0] = *reinterpret_cast<const uint32_t*>(wr + (size_t)r * DD + ca);
+        wa[r][0] = ldw4(wr + (size_t)r * DD + ca);
       }
       if constexpr (CB == 2)
-        wb[r] = *reinterpret_cast<const uint16_t*>(wr + (size_t)r * DD + cb);
+        wb[r] = ldw2(wr + (size_t)r * DD + cb);
       else
-        wb[r] = *reinterpret_cast<const uint8_t*>(wr + (size_t)r * DD + cb);
-      sa[r] = sr[(size_t)r * (DD / Q8_BLOCK) + ca / Q8_BLOCK];
-      sb[r] = sr[(size_t)r * (DD / Q8_BLOCK) + cb / Q8_BLOCK];
+        wb[r] = ldw1(wr + (size_t)r * DD + cb);
+      sa[r] = ldw2(sr + (size_t)r * (DD / Q8_BLOCK) + ca / Q8_BLOCK);
+      sb[r] = ldw2(sr + (size_t)r * (DD / Q8_BLOCK) + cb / Q8_BLOCK);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -399,14 +399,14 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
     const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
     if constexpr (FMT == FMT_BF16) {
       const uint16_t* row = static_cast<const uint16_t*>(w_up) + j * R;
-      wa[m] = *reinterpret_cast<const uint4*>(row + 8 * q);
-      wb[m] = *reinterpret_cast<const uint32_t*>(row + 256 + 2 * q);
+      wa[m] = ldw16(row + 8 * q);
+      wb[m] = ldw4(row + 256 + 2 * q);
     } else {
       const int8_t* row = static_cast<const int8_t*>(w_up) + j * R;
-      qa[m] = *reinterpret_cast<const uint2*>(row + 8 * q);
-      wb[m] = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * q);
-      sa[m] = s_up[j * (R / Q8_BLOCK) + q / 4];
-      sb[m] = s_up[j * (R / Q8_BLOCK) + 8 + q / 16];
+      qa[m] = ldw8(row + 8 * q);
+      wb[m] = ldw2(row + 256 + 2 * q);
+      sa[m] = ldw2(s_up + j * (R / Q8_BLOCK) + q / 4);
+      sb[m] = ldw2(s_up + j * (R / Q8_BLOCK) + 8 + q / 16);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
 #pragma unroll
   for (int n = 0; n < NSC; ++n) {
     const int it = min(tid + n * UPM_THREADS, SC_WORDS - 1), ss = it / (SC_WORDS / S);
-    scw[n] = reinterpret_cast<const uint32_t*>(s_up + ((size_t)ss * D + c0) * (R / Q8_BLOCK))[it % (SC_WORDS / S)];
+    scw[n] = ldw4(reinterpret_cast<const uint32_t*>(s_up + ((size_t)ss * D + c0) * (R / Q8_BLOCK)) + it % (SC_WORDS / S));
   }
   // epilogue lane: token li, column cc = 4 * wave + lg (valid when wave < 3, cc < 10 and li < T); the
   // pending loads are clamped to a valid (token, column), so that no branch separates the loads
@@ -594,15 +594,20 @@ __global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up,
   //    makes the compiler wait for them before the first barrier, serialising the weight stream with the
   //    lo staging.
   const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
+  // non-temporal weight loads (ldw*), except with a 4th wave: its repeats of the third tile's rows are separate
+  // load instructions, which then missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16)
+  constexpr bool NTW = UPM_THREADS == 192;
   const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
   uint4 a[Q8 ? 1 : R / 32];   // BF16: 8 weights per step
   uint2 qa[Q8 ? R / 32 : 1];  // Q8_0: 8 codes per step
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
     if constexpr (Q8)
-      qa[m] = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
+      qa[m] = NTW ? ldw8(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg)
+                  : *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
     else
-      a[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
+      a[m] = NTW ? ldw16(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg)
+                 : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(256) void q8_quantize(const uint4* __restrict__ w, 
 #pragma unroll
   for (int k = 0; k < Q8_CHUNKS; ++k) {
     const size_t i = i0 + k * stride;  // chunk i = block i/4, weights 8(i%4) ..
-    u[k] = (i >> 2) < n_blocks ? w[i] : make_uint4(0, 0, 0, 0);
+    u[k] = (i >> 2) < n_blocks ? ldw16(w + i) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int k = 0; k < Q8_CHUNKS; ++k) {

@@ -40,7 +40,7 @@ __device__ __forceinline__ void load_group(const uint4* __restrict__ w, int rows
 #pragma unroll
     for (int r = 0; r < MV_ROWS_PER_WAVE; ++r) {
       const int row = min(g * MV_ROWS_PER_WAVE + r, rows - 1);
-      wv[r][j] = w[(size_t)row * chunks + c];
+      wv[r][j] = ldw16(w + (size_t)row * chunks + c);
     }
   }
 }
