@@ -42,8 +42,8 @@ __device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // Weight loads: every weight is read once per call, so the loads are non-temporal (the nt bit).  Measured on
-// MI355X (cold BF16 read, one process, alternating with ordinary loads): 0.26 us faster per read on the mean
-// over T = 1..8, 0.42 us at T = 1.
+// MI355X (cold BF16 read, one process, alternating with ordinary loads): 0.26-0.33 us faster per read on the
+// mean over T = 1..8 on two boxes (on a third only T = 1 gained, 0.29 us), 10 % for the skinny matvec.
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 __device__ __forceinline__ uint4 ldw16(const void* p) {

@@ -41,8 +41,8 @@
 // issues ~100 VALU instructions per token per wave, which the loads cannot
 // hide with one wave per SIMD; the matrix-core kernel's 10 or 20 MFMAs per
 // wave cost the same at every T.  Measured on MI355X, whole read: T = 1
-// 7.03 us (v_dot2) against 7.21 (matrix cores), T = 2 7.60 against 7.56,
-// T = 8 10.42 against 9.28.
+// 6.45 us (v_dot2) against 6.82 (matrix cores); when the matrix-core kernel
+// was introduced, T = 2 7.60 against 7.56 and T = 8 10.42 against 9.28.
 //
 // T = 10..16: the down kernel takes the tokens in groups of 8 (the next
 // group's x loads overlap the current group's FMAs); up to 9 in one group.  A token's result is the
