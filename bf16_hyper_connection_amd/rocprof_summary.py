@@ -97,7 +97,23 @@ def timed_region(trace_dir):
     span = (max(int(r["End_Timestamp"]) for r in region) - min(int(r["Start_Timestamp"]) for r in region)) / 1000.0
     per_read = sorted(d + u for d, u in zip(dur["down"], dur["up"]))
     pct = {p: per_read[min(len(per_read) - 1, int(p / 100.0 * len(per_read)))] for p in (10, 50, 90)}
-    return reads, span / reads, statistics.mean(dur["down"]), statistics.mean(dur["up"]), pct
+    # per T: each down dispatch with the up dispatch that follows it (the read's two kernels, in order)
+    per_T = collections.defaultdict(list)
+    pending_down = None
+    for r in region:
+        k = kernel_key(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        if k[0] == "down":
+            pending_down = (k[1], d)
+        elif k[0] == "up" and pending_down and pending_down[0] == k[1]:
+            per_T[k[1]].append(pending_down[1] + d)
+            pending_down = None
+    return reads, span / reads, statistics.mean(dur["down"]), statistics.mean(dur["up"]), pct, per_T
+
+
+def percentiles(v):
+    v = sorted(v)
+    return [v[min(len(v) - 1, int(p / 100.0 * len(v)))] for p in (10, 50, 90)]
 
 
 def counters(d, counter):
@@ -213,7 +229,9 @@ def main():
     if tr:
         rec["timed_region"] = {"reads": tr[0], "us_per_read": round(tr[1], 3), "down_avg_us": round(tr[2], 3),
                                "up_avg_us": round(tr[3], 3),
-                               "down_plus_up_us_p10_p50_p90": [round(tr[4][p], 3) for p in (10, 50, 90)]}
+                               "down_plus_up_us_p10_p50_p90": [round(tr[4][p], 3) for p in (10, 50, 90)],
+                               "per_T_down_plus_up_us_p10_p50_p90": {str(T): [round(x, 3) for x in percentiles(v)]
+                                                                     for T, v in sorted(tr[5].items())}}
     q = ("quantize",)
     if q in dur:
         rec["q8_0_quantize"] = {"avg_us": round(dur[q][0], 3), "calls": dur[q][1],
@@ -264,6 +282,12 @@ def main():
                       f"event-timed (its `value`; {100 * tot / untraced - 100:+.1f} %)." if untraced else "")
                    + (f" Under the tracer the dispatches are spaced out: the traced run's own event figure is "
                       f"{traced:.3f} µs per read." if traced else "")]
+        if tr[5]:
+            md += ["", "Per T in the timed region, down + up per read (µs):", "",
+                   "| T | reads | p10 | p50 | p90 |", "|---|---|---|---|---|"]
+            for T, v in sorted(tr[5].items()):
+                p10, p50, p90 = percentiles(v)
+                md.append(f"| {T} | {len(v)} | {p10:.3f} | {p50:.3f} | {p90:.3f} |")
     if q in dur:
         md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
                    f"{dur[q][1]} calls."]
