@@ -147,7 +147,7 @@ def sq_table(d, commands):
             if k and k[0] in ("down", "up") and k[2] == 0 and not k[3] and not k[4]:
                 vals[(k[0], k[1])][r["Counter_Name"]].append(float(r["Counter_Value"]))
     from bf16_hyper_connection_amd.build import source_hash
-    md = ["# SQ counters of the read kernels (MI355X)", "", "Commands (from the repository root on the GPU box):",
+    md = ["# SQ counters of the read kernels (MI355X)", "", "Commands (run from the repository root, on one MI355X):",
           "", "```"] + commands + ["```", "", f"Library sources sha256 {source_hash()[:16]}…", "",
           "Medians per dispatch (BF16 weights, no pending write or injection; down = `hc_down`, up = `hc_up` at "
           "T = 1, `hc_up_mfma` from T = 2), then per wave: WAIT_ANY (waiting on anything, mostly memory), "
@@ -254,7 +254,7 @@ def main():
         json.dump(rec, fh, indent=1)
         fh.write("\n")
     md = ["# Kernel durations and HBM traffic per read (MI355X)", "",
-          "Commands (from the repository root on the GPU box):", "", "```"] + a.command + ["```", "",
+          "Commands (run from the repository root, on one MI355X):", "", "```"] + a.command + ["```", "",
           f"Counter scale from a 64 MiB device copy in the same runs: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}.",
           f"Library sources sha256 {rec['source_sha256'][:16]}…", ""] + lines
     for fname in FORMATS.values():
