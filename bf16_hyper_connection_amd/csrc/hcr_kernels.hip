@@ -7,14 +7,16 @@
 //
 //   hc_down<T>: norm statistics + down projection + split-reduction finish.
 //     A work-group owns one whole stream (2,560 columns) of 5 W_down rows, so
-//     it can apply rs itself: 8 waves (two per SIMD, so that one wave's
-//     arithmetic overlaps the other's waits), every lane owning 5 columns (an
-//     8-byte and a 2-byte piece of each row, both coalesced across the wave);
+//     it can apply rs itself: 4 waves up to 8 tokens, every lane owning 10
+//     columns (a 16-byte and a 4-byte piece of each row), and 8 waves from 9
+//     tokens (two per SIMD, so that one wave's arithmetic overlaps the other's
+//     waits), every lane owning 5 columns (an 8-byte and a 2-byte piece), all
+//     pieces coalesced across the wave;
 //     the lane computes x*w_norm and the sums of squares of its columns for
 //     the T tokens, and one FP32 FMA chain per (row, token) over the exactly
 //     widened BF16 weights.  The 6T per-lane values are summed over the wave
 //     (halving with v_permlane32/16_swap, then DPP; each group of four values
-//     as soon as its row is done) and over the 8 waves (LDS, fixed order); the
+//     as soon as its row is done) and over the waves (LDS, fixed order); the
 //     work-group writes rs[t][s] * (row sums), one partial per stream.
 //   hc_up_mfma<T, INJ, PEND> (BF16 weights from T = 2, Q8_0 copies from T = 4):
 //     lo[t][k] = the 4 stream
@@ -117,7 +119,7 @@ struct Cols {
 };
 
 template <int T, int FMT>
-__global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__ w_down,
+__global__ __launch_bounds__(down_threads(T)) void hc_down(const void* __restrict__ w_down,
                                                            const uint16_t* __restrict__ s_down,
                                                            const float* __restrict__ x,
                                                            const float* __restrict__ w_norm,
@@ -127,9 +129,9 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
   const int s = down_stream(blockIdx.x);
   const int g = down_group(blockIdx.x);  // rows DOWN_ROWS*g ..
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int CA = DOWN_CA, CB = DOWN_CB, NC = CA + CB;
-  const int ca = (2048 / DOWN_WAVES) * wave + CA * lane;        // CA columns: one 2*CA-byte chunk per row
-  const int cb = 2048 + (512 / DOWN_WAVES) * wave + CB * lane;  // CB columns
+  constexpr int WAVES = down_waves(T), CA = down_ca(T), CB = down_cb(T), NC = CA + CB;
+  const int ca = (2048 / WAVES) * wave + CA * lane;        // CA columns: one 2*CA-byte chunk per row
+  const int cb = 2048 + (512 / WAVES) * wave + CB * lane;  // CB columns
 
   // Up to 9 tokens are taken in one group (every x load issued up front); from 10 tokens in groups of 8 (x of
   // one group in registers at a time, the next group's loads under this group's FMAs).  Measured on MI355X
@@ -284,6 +286,10 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
           }
         }
       }
+      // four waves: row by row (the compiler would otherwise merge the waits of the last rows' loads at
+      // T = 5..7, so that their FMAs wait for all of them; with the barrier they wait row by row as with
+      // eight waves, measured 0.2-0.3 us faster per read at T = 5..7)
+      if constexpr (WAVES == 4) __builtin_amdgcn_sched_barrier(0);
       if constexpr (EARLY) {  // 4. sums over the wave of the quadruples this row completes
 #pragma unroll
         for (int q = quads_known(r); q < quads_known(r + 1); ++q) wave_quad_sum<N>(v, q);
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
 
   // 4. sums over the wave (several token groups: all at the end), then over the waves in a fixed order
   if constexpr (!EARLY) wave_sum<N>(v);
-  __shared__ float wsum[DOWN_WAVES][N];
+  __shared__ float wsum[WAVES][N];
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) wsum[wave][(lane >> 4) * (N / 4) + i] = v[i];
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void hc_down(const void* __restrict__
     const int pr = quad_pos((r + 1) * T + t, N), pq = quad_pos(t, N);
     float a = wsum[0][pr], q = wsum[0][pq];
 #pragma unroll
-    for (int k = 1; k < DOWN_WAVES; ++k) {
+    for (int k = 1; k < WAVES; ++k) {
       a += wsum[k][pr];
       q += wsum[k][pq];
     }
@@ -793,7 +799,7 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   float* lo = reinterpret_cast<float*>(sc + OFF_LO);
   float* rs = reinterpret_cast<float*>(sc + OFF_RS);
   (void)hipGetLastError();  // clear a stale error left by unrelated earlier calls
-  hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(DOWN_THREADS), 0, st, w_down, s_down, x, w_norm, part,
+  hipLaunchKernelGGL(kDown[fmt][T - 1], dim3(DOWN_WGS), dim3(down_threads(T)), 0, st, w_down, s_down, x, w_norm, part,
                      rs);
   const bool mfma = T >= (fmt == FMT_BF16 ? UP_MFMA_FROM : UP_MFMA_FROM_Q8);
   const up_fn up = mfma ? kUpM[fmt][T - 1][inj != nullptr][pending != nullptr]

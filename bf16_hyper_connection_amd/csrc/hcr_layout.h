@@ -20,19 +20,31 @@ constexpr int DD = S * D;          // 10240: down K = up rows
 // contiguous, so that the 128-byte lines the work-groups share (rows of partials; pending, out and mean)
 // stay in one L2
 constexpr int XCDS = 8;
-// ---- down kernel: one work-group = one stream (2,560 columns) x 5 rows of W_down; 8 waves (two
-// per SIMD), lane l of wave w owns stream columns [256w + 4l, +4) and 2048 + 64w + l
+// ---- down kernel: one work-group = one stream (2,560 columns) x 5 rows of W_down, with down_waves(T)
+// waves: lane l of wave w owns stream columns [(2048 / W) w + CA l, +CA) and 2048 + (512 / W) w + CB l
+// (W = 4: 8 and 2 columns, one wave per SIMD; W = 8: 4 and 1 columns, two waves per SIMD)
 constexpr int DOWN_ROWS = 5;
 constexpr int DOWN_WGS = S * (R / DOWN_ROWS);  // 256
 // down work-group b: stream b mod 4 (XCDs k and k + 4 serve stream k), row group g; XCD k takes row groups
 // 0 .. 31 of its stream and XCD k + 4 row groups 32 .. 63
 constexpr int down_stream(int b) { return b % S; }
 constexpr int down_group(int b) { return ((b % XCDS) / S) * (DOWN_WGS / XCDS) + b / XCDS; }
-constexpr int DOWN_WAVES = 8;
-constexpr int DOWN_THREADS = 64 * DOWN_WAVES;
-constexpr int DOWN_CA = 32 / DOWN_WAVES, DOWN_CB = 8 / DOWN_WAVES;  // a lane's columns per row: CA at ca, CB at cb
-static_assert((DOWN_WAVES == 4 || DOWN_WAVES == 8) && DOWN_CA * 64 * DOWN_WAVES == 2048 &&
-              DOWN_CB * 64 * DOWN_WAVES == 512, "the down kernel's column runs must tile the stream");
+// Four waves up to 8 tokens, eight from 9 (T = 9..16 share one width, so that a token's result does not
+// depend on T within that range).  Measured on MI355X (whole read, one process, alternating, 3 rounds):
+// four waves were 0.04-0.15 us faster per read at every T = 1..8 (BF16 mean 7.56 against 7.66 us, Q8_0
+// 7.74 against 7.82 us) and 0.2-0.6 us slower at T = 11..16
+constexpr int down_waves(int T) { return T <= 8 ? 4 : 8; }
+constexpr int down_threads(int T) { return 64 * down_waves(T); }
+constexpr int down_ca(int T) { return 32 / down_waves(T); }  // a lane's columns per row: CA at ca, CB at cb
+constexpr int down_cb(int T) { return 8 / down_waves(T); }
+constexpr bool down_tiles_ok() {
+  for (int T = 1; T <= TMAX; ++T) {
+    const int w = down_waves(T);
+    if ((w != 4 && w != 8) || down_ca(T) * 64 * w != 2048 || down_cb(T) * 64 * w != 512) return false;
+  }
+  return true;
+}
+static_assert(down_tiles_ok(), "the down kernel's column runs must tile the stream");
 // ---- up kernel: one work-group = 10 columns x 4 streams = 40 rows of W_up, 4 waves of 10 rows;
 // a row is reduced by the 32 lanes of a half-wave, lane q owning K [8q, 8q+8) and [256 + 2q, +2)
 constexpr int UP_COLS = 10;
@@ -85,9 +97,9 @@ static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0,
 // ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
 enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
 constexpr int Q8_BLOCK = 32;
-static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % DOWN_CA == 0 &&
-                  Q8_BLOCK % 8 == 0,
-              "each of a lane's column runs (down: DOWN_CA and DOWN_CB columns; up: 8 and 2) must sit inside one "
+static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % down_ca(1) == 0 &&
+                  Q8_BLOCK % down_ca(TMAX) == 0 && Q8_BLOCK % 8 == 0,
+              "each of a lane's column runs (down: down_ca and down_cb columns; up: 8 and 2) must sit inside one "
               "Q8_0 block");
 
 // Enqueue the two kernels of one read (T in 1..TMAX; arguments already validated).  For
