@@ -286,10 +286,11 @@ __global__ __launch_bounds__(down_threads(T)) void hc_down(const void* __restric
           }
         }
       }
-      // four waves: row by row (the compiler would otherwise merge the waits of the last rows' loads at
-      // T = 5..7, so that their FMAs wait for all of them; with the barrier they wait row by row as with
-      // eight waves, measured 0.2-0.3 us faster per read at T = 5..7)
-      if constexpr (WAVES == 4) __builtin_amdgcn_sched_barrier(0);
+      // row by row: without this barrier the compiler merged the waits for several rows' loads (four waves
+      // at T = 5..7, eight waves with token groups), so that early rows' FMAs waited for later rows' weights.
+      // Measured (one process, alternating, 3 rounds): 0.2-0.3 us faster per read at T = 5..7 with four
+      // waves, 0.05-0.16 us at T = 10..15 with eight, level at T = 9 and 16
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (EARLY) {  // 4. sums over the wave of the quadruples this row completes
 #pragma unroll
         for (int q = quads_known(r); q < quads_known(r + 1); ++q) wave_quad_sum<N>(v, q);
