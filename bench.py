@@ -80,27 +80,123 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(budget_s=12.0):
-    """The FP64 reference, as it stands, on a bounded sample of the same sweep (host cores)."""
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(budget_s=8.0):
+    """The FP64 reference, as it stands, on a bounded sample of the same sweep: once on the host's BLAS
+    threads, once on one core (BLAS limited to one thread)."""
     import oracle
     from bf16_hyper_connection_amd import inputs as gen
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        threadpool_limits, threads = None, 1
     ws = [gen.weight_set(2, k) for k in range(4)]
     xs = {T: gen.cold_sweep_x(T) for T in range(1, TMAX + 1)}
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        for T in range(1, TMAX + 1):
-            w = ws[n % len(ws)]
-            oracle.hc_read(xs[T], w.w_norm, w.w_down, w.w_up)
-            n += 1
-    el = time.perf_counter() - t0
-    return {"value": round(el / n * 1e6, 1), "unit": "µs per read", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} reads of the same sweep (T = 1..8 in turn, 4 of the 32 weight sets), "
-                      f"{el:.1f} s of float64 numpy on the host"}
+
+    def run(budget):
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            for T in range(1, TMAX + 1):
+                w = ws[n % len(ws)]
+                oracle.hc_read(xs[T], w.w_norm, w.w_down, w.w_up)
+                n += 1
+        return n, time.perf_counter() - t0
+
+    n, el = run(budget_s)
+    res = {"value": round(el / n * 1e6, 1), "unit": "µs per read", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} reads of the same sweep (T = 1..8 in turn, 4 of the 32 weight sets), "
+                     f"{el:.1f} s of float64 numpy on the host",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            n1, el1 = run(budget_s)
+        res["one_core"] = {"value": round(el1 / n1 * 1e6, 1), "unit": "µs per read", "cores": 1,
+                           "sample": f"{n1} reads of the same sweep, {el1:.1f} s, BLAS limited to one thread"}
+    return res
+
+
+def calib_lib():
+    """libhcr_calib.so (include/hcr_calib.h): the read's two launches empty, and with only their loads."""
+    import ctypes
+    from bf16_hyper_connection_amd import build
+    if not os.path.exists(build.CALIB_LIB):
+        raise RuntimeError(f"{build.CALIB_LIB} is missing: build first")
+    L = ctypes.CDLL(build.CALIB_LIB)
+    vp = ctypes.c_void_p
+    L.hcrc_read_floor.restype = ctypes.c_int
+    L.hcrc_read_floor.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    return L
+
+
+def ab_compare(args, readers, xs, outs, means, stream, timed):
+    """Time the per-T cold sweep through several builds of libhcr.so (same C ABI), alternating between
+    them round by round in one process; returns the comparison (median µs per read per T and library)."""
+    import ctypes
+    import torch
+    Ts = list(range(1, args.ab_tmax + 1))
+    libs = []
+    for path in args.ab:
+        L = ctypes.CDLL(os.path.abspath(path), mode=os.RTLD_LOCAL)
+        vp = ctypes.c_void_p
+        L.hcr_scratch_bytes.restype, L.hcr_scratch_bytes.argtypes = ctypes.c_size_t, []
+        L.hcr_create.restype, L.hcr_create.argtypes = ctypes.c_int, [vp, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.hcr_read.restype, L.hcr_read.argtypes = ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+        nb = L.hcr_scratch_bytes()
+        handles, scratch = [], []
+        for r in readers:
+            sc = torch.empty(nb, dtype=torch.uint8, device=r.w_down.device)
+            h = vp()
+            rc = L.hcr_create(r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(), sc.data_ptr(), nb,
+                              ctypes.byref(h))
+            assert rc == 0, (path, rc)
+            handles.append(h)
+            scratch.append(sc)
+        graphs = {}
+        for T in Ts:
+            g = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for h in handles:
+                        rc = L.hcr_read(h, T, xs[T].data_ptr(), None, None, outs[T].data_ptr(), means[T].data_ptr(),
+                                        vp(stream.cuda_stream))
+                        assert rc == 0, (path, T, rc)
+            torch.cuda.current_stream().wait_stream(stream)
+            graphs[T] = g
+        libs.append((os.path.basename(path), L, handles, scratch, graphs))
+    times = {name: {T: [] for T in Ts} for name, *_ in libs}
+    for rnd in range(args.ab_rounds):
+        for name, L, handles, scratch, graphs in libs:
+            for T in Ts:
+                times[name][T].append(timed(graphs[T], args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(handles)))
+            log(f"bench: A/B round {rnd} {name}: " + " ".join(f"{times[name][T][-1]:.3f}" for T in Ts))
+    res = {}
+    for name in times:
+        med = {T: round(float(np.median(times[name][T])), 3) for T in Ts}
+        res[name] = {"per_T_us": med, "mean_us": round(sum(med.values()) / len(med), 3),
+                     "per_T_spread_us": {T: round(max(v) - min(v), 3) for T, v in times[name].items()}}
+    return res
+
+
+def sha256_of(*tensors):
+    """sha256 (hex) of the bytes of device tensors, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.detach().contiguous().cpu().numpy().tobytes())
+    return h.hexdigest()
 
 
 def main():
@@ -114,6 +210,13 @@ def main():
     ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0 copies' per-T measurement")
     ap.add_argument("--per-t-reps", type=int, default=10, help="graph replays per T for the per-T figures")
     ap.add_argument("--no-matvec", action="store_true", help="skip the skinny BF16 matvec measurement")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the calibration leg (the read's two launches empty, and with only their loads)")
+    ap.add_argument("--ab", nargs="+", metavar="LIB",
+                    help="A/B mode: time the per-T sweep through each of these builds of libhcr.so in turn "
+                         "(alternating, --ab-rounds rounds), print one JSON line of the comparison and exit")
+    ap.add_argument("--ab-rounds", type=int, default=3)
+    ap.add_argument("--ab-tmax", type=int, default=8, help="A/B mode: T = 1..this")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -178,8 +281,18 @@ def main():
             torch.cuda.synchronize()
         return e0.elapsed_time(e1)  # ms
 
+    if args.ab:
+        res = ab_compare(args, readers, xs, outs, means, stream, timed)
+        print(json.dumps({"ab": res, "rounds": args.ab_rounds, "weight_sets": len(readers),
+                          "note": "median µs per read over the rounds, cold 32-set rotation, libraries alternating"}),
+              flush=True)
+        return
+
     # per-T: 32 rotated reads per graph, replayed 10 times (320 calls per T); T = 9..16 reported beside
-    per_T_us, per_T_gbps = {}, {}
+    # The output hashes: after the replays, out and mean hold the last read of the graph (the last weight
+    # set); the same read made directly must give the same bytes
+    per_T_us, per_T_gbps, hashes = {}, {}, {"cold_sweep": {}}
+    replay_equals_direct = True
     for T in range(1, T_WIDE + 1):
         g = capture([T], len(readers))
         ms = timed(g, args.per_t_reps, 2)
@@ -188,6 +301,11 @@ def main():
         per_T_gbps[T] = round(algorithmic_bytes(T) / us / 1e3, 1)
         log(f"bench: T={T} {us:.3f} us/read  {per_T_gbps[T]:.0f} GB/s")
         del g
+        h_out, h_mean = sha256_of(outs[T]), sha256_of(means[T])
+        d_out, d_mean = readers[-1].read(xs[T])
+        torch.cuda.synchronize()
+        replay_equals_direct &= (sha256_of(d_out), sha256_of(d_mean)) == (h_out, h_mean)
+        hashes["cold_sweep"][T] = {"out": h_out, "mean": h_mean}
 
     # cold-cache check: T = 1 and T = 8 with 1 weight set (MALL- and L2-resident), the 32 sets, and 64 sets
     # (the 32 and copies of them in other memory); 32 and 64 must agree if the rotation defeats the MALL
@@ -209,6 +327,34 @@ def main():
         log(f"bench: cold check T={T}: {row}")
     del extra
 
+    # the calibration leg: the read's two launches on the same grids and the same 32 rotated sets, empty, and
+    # with only their global loads (include/hcr_calib.h), per T
+    calibration = None
+    if not args.no_calibration:
+        cal = calib_lib()
+        calibration = {"empty_pair_us": {}, "loads_pair_us": {}}
+        for kind, key in ((0, "empty_pair_us"), (1, "loads_pair_us")):
+            for T in range(1, T_WIDE + 1):
+                gk = torch.cuda.CUDAGraph()
+                stream.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(stream):
+                    with torch.cuda.graph(gk, stream=stream):
+                        for r in readers:
+                            rc = cal.hcrc_read_floor(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(),
+                                                     r.w_norm.data_ptr(), r.scratch.data_ptr(), xs[T].data_ptr(),
+                                                     stream.cuda_stream)
+                            assert rc == hcr.HCR_OK, rc
+                torch.cuda.current_stream().wait_stream(stream)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                del gk
+            log(f"bench: calibration {key}: {calibration[key]}")
+        calibration["read_over_loads_us"] = {T: round(per_T_us[T] - calibration["loads_pair_us"][T], 3)
+                                             for T in range(1, T_WIDE + 1)}
+        calibration["note"] = ("per T, graphs of 32 pairs on the read's grids and work-group sizes over the 32 rotated "
+                               "weight sets, replayed like the per-T figures: empty_pair = two empty kernels, "
+                               "loads_pair = the read's global loads only (same order, widths and cache policy; no "
+                               "arithmetic, LDS, barrier or store); read_over_loads = per_T_us - loads_pair")
+
     # the full epilogue (pending write and injection on) over the same 32 rotated weight sets: T = 4 with the
     # seeded x, pending and injection of the full-epilogue workload, and T = 8 with those of the numerics-stress
     # workload (heavy-tailed x); the weight values do not change the time of a read
@@ -227,6 +373,11 @@ def main():
         us = timed(ge, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers))
         full_epilogue[T] = {"us_per_read": round(us, 3),
                             "algorithmic_GBps": round(algorithmic_bytes(T, pending=True, inj=True) / us / 1e3, 1)}
+        hashes.setdefault("full_epilogue", {})[T] = {"out": sha256_of(outs[T]), "mean": sha256_of(means[T])}
+        d_out, d_mean = readers[-1].read(ex[-1], ep[-1], ei[-1])
+        torch.cuda.synchronize()
+        replay_equals_direct &= (sha256_of(d_out), sha256_of(d_mean)) == (hashes["full_epilogue"][T]["out"],
+                                                                          hashes["full_epilogue"][T]["mean"])
         log(f"bench: full epilogue T={T} {us:.3f} us/read")
         del ge, ex, ep, ei
     full_epilogue["note"] = ("pending write and injection on, 32 rotated weight sets; T = 4: the full-epilogue "
@@ -294,6 +445,8 @@ def main():
             us = timed(gq, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(q8_readers))
             q8_T_us[T] = round(us, 3)
             q8_T_gbps[T] = round(algorithmic_bytes_q8(T) / us / 1e3, 1)
+            if T <= TMAX:
+                hashes.setdefault("q8_0", {})[T] = {"out": sha256_of(outs[T]), "mean": sha256_of(means[T])}
             log(f"bench: Q8_0 T={T} {us:.3f} us/read  {q8_T_gbps[T]:.0f} GB/s")
             del gq
         mean_us = sum(q8_T_us[T] for T in range(1, TMAX + 1)) / TMAX
@@ -370,6 +523,8 @@ def main():
         torch.cuda.current_stream().wait_stream(stream)
         reps = 50
         wms = timed(gw, reps, 3) / reps
+        hashes["verify_window"] = {"out_last": sha256_of(wouts[-1]), "mean_last": sha256_of(wmeans[-1]),
+                                   "means_all": sha256_of(*wmeans)}
         wbytes = n_win * algorithmic_bytes(t_win, pending=True)
         window = {"reads": n_win, "T": t_win, "pending": True, "us_per_window": round(wms * 1000, 2),
                   "us_per_read": round(wms * 1000 / n_win, 3),
@@ -413,8 +568,13 @@ def main():
                                           "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items()
                                                                      if T > TMAX},
                                           "note": "same cold rotation, not part of the timed step"},
-                   "cold_cache_check_us_per_read": cold_check, "full_epilogue": full_epilogue,
-                   "verify_window": window, "q8_0": q8, "matvec_bf16": matvec},
+                   "cold_cache_check_us_per_read": cold_check, "calibration": calibration,
+                   "full_epilogue": full_epilogue,
+                   "verify_window": window, "q8_0": q8, "matvec_bf16": matvec,
+                   "output_sha256": hashes, "replay_equals_direct": bool(replay_equals_direct),
+                   "output_sha256_note": "sha256 of the bytes of out and of mean after each graph (the last read: "
+                                         "the last weight set); replay_equals_direct: the same reads made directly "
+                                         "gave the same bytes"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "the read (hc_down + hc_up_mfma / hc_up dispatches), event-timed per read over the "

@@ -1,0 +1,219 @@
+// Calibration kernels of the BF16 hyper-connection read (libhcr_calib.so, include/hcr_calib.h):
+// the read's two launches with nothing in them (HCRC_EMPTY), and with only their global loads
+// (HCRC_LOADS).  Measurement only.
+//
+// The load kernels repeat the index arithmetic of hc_down<T, FMT_BF16> and of the up kernel the read
+// dispatches at T (hc_up at T = 1, hc_up_mfma from T = 2) in hcr_kernels.hip: the same work-group
+// maps (down_stream / down_group, up_tile), lane ownership, load widths, load order and cache policy
+// (non-temporal weight loads).  Every loaded register is handed to an empty asm statement, so the
+// compiler keeps the load and waits for it, and nothing else is done with it.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hcr_calib.h"
+#include "hcr_device.h"
+#include "hcr_layout.h"
+
+namespace hcr {
+namespace {
+
+__device__ __forceinline__ void use(uint32_t v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void use(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void use(f32x4 v) {
+  use(v[0]), use(v[1]), use(v[2]), use(v[3]);
+}
+__device__ __forceinline__ void use(uint4 v) { use(v.x), use(v.y), use(v.z), use(v.w); }
+__device__ __forceinline__ void use(uint2 v) { use(v.x), use(v.y); }
+
+__global__ void cal_empty() {}
+
+// hc_down<T>'s loads: the stream's x (token groups of 8 from T = 10, the next group's loads issued
+// before the current group is consumed), w_norm, then the 5 weight rows
+template <int CA, int CB>
+struct ColsRaw {
+  f32x4 a[CA / 4];
+  float b[CB];
+  __device__ __forceinline__ void load(const float* p, int ca, int cb) {
+#pragma unroll
+    for (int e = 0; e < CA / 4; ++e) a[e] = ld4(p + ca + 4 * e);
+    if constexpr (CB == 2) {
+      const f32x2 v = ld2(p + cb);
+      b[0] = v[0], b[1] = v[1];
+    } else {
+      b[0] = p[cb];
+    }
+  }
+  __device__ __forceinline__ void consume() const {
+#pragma unroll
+    for (int e = 0; e < CA / 4; ++e) use(a[e]);
+#pragma unroll
+    for (int e = 0; e < CB; ++e) use(b[e]);
+  }
+};
+
+template <int T>
+__global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t* __restrict__ w_down,
+                                                                  const float* __restrict__ x,
+                                                                  const float* __restrict__ w_norm) {
+  const int s = down_stream(blockIdx.x), g = down_group(blockIdx.x);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int WAVES = down_waves(T), CA = down_ca(T), CB = down_cb(T);
+  const int ca = (2048 / WAVES) * wave + CA * lane;
+  const int cb = 2048 + (512 / WAVES) * wave + CB * lane;
+  constexpr int TG = T <= 9 ? T : 8;
+  constexpr int NG = (T + TG - 1) / TG;
+  ColsRaw<CA, CB> xv[TG];
+  auto load_x = [&](int grp) {
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+      const int t = grp * TG + i;
+      if (t < T) xv[i].load(x + ((size_t)t * S + s) * D, ca, cb);
+    }
+  };
+  load_x(0);
+  ColsRaw<CA, CB> nv;
+  nv.load(w_norm + s * D, ca, cb);
+  uint32_t wa[DOWN_ROWS][CA / 2], wb[DOWN_ROWS];
+  const uint16_t* wr = w_down + (size_t)(DOWN_ROWS * g) * DD + (size_t)s * D;
+#pragma unroll
+  for (int r = 0; r < DOWN_ROWS; ++r) {
+    if constexpr (CA == 8) {
+      const uint4 v = ldw16(wr + (size_t)r * DD + ca);
+      wa[r][0] = v.x, wa[r][1] = v.y, wa[r][2] = v.z, wa[r][3] = v.w;
+    } else {
+      const uint2 v = ldw8(wr + (size_t)r * DD + ca);
+      wa[r][0] = v.x, wa[r][1] = v.y;
+    }
+    wb[r] = CB == 2 ? ldw4(wr + (size_t)r * DD + cb) : ldw2(wr + (size_t)r * DD + cb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+#pragma unroll
+    for (int i = 0; i < TG; ++i)
+      if (grp * TG + i < T) xv[i].consume();
+    if (grp == 0) nv.consume();
+    if (grp + 1 < NG) load_x(grp + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) {
+#pragma unroll
+      for (int r = 0; r < DOWN_ROWS; ++r) {
+#pragma unroll
+        for (int e = 0; e < CA / 2; ++e) use(wa[r][e]);
+        use(wb[r]);
+      }
+    }
+  }
+}
+
+// hc_up_mfma<T>'s loads (T >= 2): partials, then one 16-row tile of W_up per wave, 10 K steps
+template <int T>
+__global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
+                                                         const float* __restrict__ part) {
+  constexpr int NT = upm_threads(T);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c0 = up_tile(blockIdx.x) * UP_COLS;
+  const int li = lane & 15, lg = lane >> 4;
+  const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
+  const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+  constexpr bool NTW = NT == 192;
+  // the partials first (issued before the weights, consumed after them, as in the read)
+  constexpr int ITEMS = T * (R / 4);
+  constexpr int NI = (ITEMS + NT - 1) / NT;
+  f32x4 pv[NI][S];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it = min(tid + n * NT, ITEMS - 1);
+    const int t = it / (R / 4), k = 4 * (it % (R / 4));
+#pragma unroll
+    for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 a[R / 32];
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m)
+    a[m] = NTW ? ldw16(w_up + j * R + 32 * m + 8 * lg) : *reinterpret_cast<const uint4*>(w_up + j * R + 32 * m + 8 * lg);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NI; ++n)
+#pragma unroll
+    for (int ss = 0; ss < S; ++ss) use(pv[n][ss]);
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m) use(a[m]);
+}
+
+// hc_up<1>'s loads: partials, then 5 iterations of two rows per wave (16 + 4 bytes per lane and row)
+__global__ __launch_bounds__(UP_THREADS) void cal_up1_loads(const uint16_t* __restrict__ w_up,
+                                                            const float* __restrict__ part) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, q = lane & 31;
+  const int c0 = up_tile(blockIdx.x) * UP_COLS;
+  constexpr int ITEMS = R / 4;
+  const int it = min(tid, ITEMS - 1), k = 4 * it;
+  f32x4 pv[S];
+#pragma unroll
+  for (int ss = 0; ss < S; ++ss) pv[ss] = ld4(part + (size_t)ss * TMAX * R + k);
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wa[UP_ITERS];
+  uint32_t wb[UP_ITERS];
+#pragma unroll
+  for (int m = 0; m < UP_ITERS; ++m) {
+    const int rw = UP_WAVE_ROWS * wave + 2 * m + h;
+    const uint16_t* row = w_up + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
+    wa[m] = ldw16(row + 8 * q);
+    wb[m] = ldw4(row + 256 + 2 * q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ss = 0; ss < S; ++ss) use(pv[ss]);
+#pragma unroll
+  for (int m = 0; m < UP_ITERS; ++m) use(wa[m]), use(wb[m]);
+}
+
+typedef void (*cal_down_fn)(const uint16_t*, const float*, const float*);
+typedef void (*cal_up_fn)(const uint16_t*, const float*);
+static_assert(TMAX == 16, "the tables below list T = 1..16");
+const cal_down_fn kCalDown[TMAX] = {cal_down_loads<1>,  cal_down_loads<2>,  cal_down_loads<3>,  cal_down_loads<4>,
+                                    cal_down_loads<5>,  cal_down_loads<6>,  cal_down_loads<7>,  cal_down_loads<8>,
+                                    cal_down_loads<9>,  cal_down_loads<10>, cal_down_loads<11>, cal_down_loads<12>,
+                                    cal_down_loads<13>, cal_down_loads<14>, cal_down_loads<15>, cal_down_loads<16>};
+const cal_up_fn kCalUp[TMAX] = {cal_up1_loads,          cal_up_mfma_loads<2>,  cal_up_mfma_loads<3>,
+                                cal_up_mfma_loads<4>,   cal_up_mfma_loads<5>,  cal_up_mfma_loads<6>,
+                                cal_up_mfma_loads<7>,   cal_up_mfma_loads<8>,  cal_up_mfma_loads<9>,
+                                cal_up_mfma_loads<10>,  cal_up_mfma_loads<11>, cal_up_mfma_loads<12>,
+                                cal_up_mfma_loads<13>,  cal_up_mfma_loads<14>, cal_up_mfma_loads<15>,
+                                cal_up_mfma_loads<16>};
+static_assert(UP_MFMA_FROM == 2, "the read dispatches hc_up at T = 1 and hc_up_mfma from T = 2");
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+}  // namespace
+}  // namespace hcr
+
+extern "C" int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
+                               const void* scratch, const float* x, void* stream) {
+  using namespace hcr;
+  if ((kind != HCRC_EMPTY && kind != HCRC_LOADS) || T < 1 || T > TMAX) return HCR_EINVAL;
+  if (kind == HCRC_LOADS) {
+    if (!w_down || !w_up || !w_norm || !scratch || !x) return HCR_EINVAL;
+    if (!aligned(w_down, 16) || !aligned(w_up, 16) || !aligned(w_norm, 16) || !aligned(scratch, 256) ||
+        !aligned(x, 16))
+      return HCR_EALIGN;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const unsigned up_threads = T >= UP_MFMA_FROM ? upm_threads(T) : UP_THREADS;
+  (void)hipGetLastError();
+  if (kind == HCRC_EMPTY) {
+    hipLaunchKernelGGL(cal_empty, dim3(DOWN_WGS), dim3(down_threads(T)), 0, st);
+    hipLaunchKernelGGL(cal_empty, dim3(UP_WGS), dim3(up_threads), 0, st);
+  } else {
+    const float* part = reinterpret_cast<const float*>(static_cast<const char*>(scratch) + OFF_PART);
+    hipLaunchKernelGGL(kCalDown[T - 1], dim3(DOWN_WGS), dim3(down_threads(T)), 0, st,
+                       static_cast<const uint16_t*>(w_down), x, w_norm);
+    hipLaunchKernelGGL(kCalUp[T - 1], dim3(UP_WGS), dim3(up_threads), 0, st, static_cast<const uint16_t*>(w_up),
+                       part);
+  }
+  return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}

@@ -98,7 +98,10 @@ int hcr_create(const void* w_down, const void* w_up, const float* w_norm,
  *
  * hcr_quantize_q8_0: make the Q8_0 copy of a row-major BF16 matrix w
  * [rows][cols] (cols a multiple of 32; weights finite) on the device,
- * asynchronously on `stream` (one kernel; no allocation).  The codes and the
+ * asynchronously on `stream` (one kernel; no allocation).  Finite scales need
+ * every block's largest |w| to be at most 127 * 65504 = 8,319,008 (65504 is
+ * binary16's largest finite value): beyond it d rounds to +inf in binary16, the
+ * call still returns HCR_OK, and a read on such copies has non-finite outputs.  The codes and the
  * scales are bitwise those of the rule above.  For the read, W_down is
  * [320][10240] and W_up is [10240][320].  Pointers are device pointers the
  * caller owns, 16-byte aligned, and codes, scales and w must not overlap.

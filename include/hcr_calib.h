@@ -1,0 +1,51 @@
+/*
+ * hcr_calib.h -- C ABI of the calibration kernels of the BF16 hyper-connection
+ * read (libhcr_calib.so).  Measurement only: nothing here computes the read.
+ *
+ * The read (include/hcr.h; Strata PR #2812, "sycl: STRATA_GR_FUSED=1, the
+ * two-kernel BF16 hyper-connection read (opt-in)", What changed: one kernel for
+ * the norm, the down projection and its split-reduction finish, a second for the
+ * up projection and the epilogue) costs two dependent launches that each stream
+ * one 6.55 MB BF16 matrix.  These kernels give the floor of that structure on
+ * the machine at hand, per T:
+ *
+ *   HCRC_EMPTY  two empty kernels with the grids and work-group sizes of the
+ *               read's two launches at T;
+ *   HCRC_LOADS  two kernels with the same grids and work-group sizes that issue
+ *               exactly the read's global loads at T, in the same order and with
+ *               the same cache policy (down: the stream's x for the T tokens,
+ *               w_norm, then the work-group's 5 rows of W_down; up: the 4 stream
+ *               partials of lo, then the work-group's 40 rows of W_up), wait for
+ *               every loaded value and discard it: no arithmetic, no LDS, no
+ *               barrier, no store.
+ *
+ * The difference between the read and HCRC_LOADS is what the read's arithmetic,
+ * reductions, LDS staging, barriers and stores add to its bare memory traffic.
+ *
+ * hcrc_read_floor: enqueue the pair `kind` for T tokens (1..HCR_T_MAX) on
+ * `stream` (a hipStream_t; NULL is the null stream).  The pointers are those of
+ * a read (include/hcr.h layouts): w_down and w_up BF16, w_norm float [4][2560],
+ * scratch of hcr_scratch_bytes() bytes (its partials are loaded, never written),
+ * x float [T][4][2560]; all device pointers, 16-byte aligned (scratch 256),
+ * only read.  HCRC_EMPTY ignores them (they may be NULL).  No allocation, no
+ * memset; graph-capturable.
+ * Errors: HCR_EINVAL (unknown kind, T out of range, a NULL pointer for
+ * HCRC_LOADS), HCR_EALIGN (both before any HIP call), HCR_EHIP.
+ */
+#ifndef HCR_CALIB_H
+#define HCR_CALIB_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { HCRC_EMPTY = 0, HCRC_LOADS = 1 };
+
+int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
+                    const void* scratch, const float* x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCR_CALIB_H */

@@ -1,0 +1,80 @@
+"""libhcr_calib.so (include/hcr_calib.h), the calibration kernels of bench.py: it loads, exports what its
+header declares and rejects bad arguments before any HIP call (CPU); on the GPU both pairs run."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bf16_hyper_connection_amd import build
+from tests.libhcr_util import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "hcr_calib.h")
+HCR_OK, HCR_EINVAL, HCR_EALIGN = 0, -1, -2
+
+
+@pytest.fixture(scope="module")
+def cal():
+    ensure_built()
+    if not os.path.exists(build.CALIB_LIB):
+        build.build()
+    L = ctypes.CDLL(build.CALIB_LIB)
+    vp = ctypes.c_void_p
+    L.hcrc_read_floor.restype = ctypes.c_int
+    L.hcrc_read_floor.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    return L
+
+
+def test_exports_every_declared_symbol(cal):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(hcrc_[a-z_]+)\s*\(", text)))
+    assert names == ["hcrc_read_floor"]
+    for n in names:
+        assert hasattr(cal, n)
+
+
+FAKE = dict(wd=0x10000000, wu=0x20000000, wn=0x30000000, sc=0x40000000, x=0x50000000)
+
+
+@pytest.mark.parametrize("kind,T,kw,rc", [
+    (2, 1, {}, HCR_EINVAL),            # unknown kind
+    (-1, 1, {}, HCR_EINVAL),
+    (0, 0, {}, HCR_EINVAL),            # T out of range
+    (1, 17, {}, HCR_EINVAL),
+    (1, 1, dict(wd=None), HCR_EINVAL),
+    (1, 1, dict(x=None), HCR_EINVAL),
+    (1, 1, dict(sc=None), HCR_EINVAL),
+    (1, 1, dict(wu=0x20000008), HCR_EALIGN),
+    (1, 1, dict(sc=0x40000010), HCR_EALIGN),
+    (1, 1, dict(x=0x50000004), HCR_EALIGN),
+])
+def test_rejects_before_any_hip_call(cal, kind, T, kw, rc):
+    a = dict(FAKE)
+    a.update(kw)
+    assert cal.hcrc_read_floor(kind, T, a["wd"], a["wu"], a["wn"], a["sc"], a["x"], None) == rc
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 2, 8, 9, 10, 16])
+def test_pairs_run_and_write_nothing(cal, T):
+    import numpy as np
+    import torch
+
+    from bf16_hyper_connection_amd import hcr
+    from bf16_hyper_connection_amd import inputs as gen
+    from tests.gpu_util import reader_for, to_dev
+
+    print(f"calibration pairs T={T}", flush=True)
+    r = reader_for(gen.weight_set(0, 0))
+    x = to_dev(gen.activations(0, T))
+    snap = [t.clone() for t in (r.w_down, r.w_up, r.w_norm, r.scratch, x)]
+    st = torch.cuda.current_stream().cuda_stream
+    for kind in (0, 1):
+        rc = cal.hcrc_read_floor(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(),
+                                 r.scratch.data_ptr(), x.data_ptr(), st)
+        assert rc == HCR_OK, hcr.hcr_strerror(rc)
+    torch.cuda.synchronize()
+    for a, b in zip(snap, (r.w_down, r.w_up, r.w_norm, r.scratch, x)):
+        assert torch.equal(a, b)
+    assert np.isfinite(x.cpu().numpy()).all()

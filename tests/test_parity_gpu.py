@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from bf16_hyper_connection_amd import hcr
 from bf16_hyper_connection_amd import inputs as gen
 from tests import oracle_pins as pins
 from tests.gpu_util import check_read, dev, reader_for, to_dev
@@ -147,12 +148,23 @@ def test_all_zero_input(wset):
 
 
 def test_empty_read_leaves_outputs(wset):
+    """T = 0 enqueues nothing: non-empty out, mean and scratch filled with sentinels keep every byte."""
     _, reader = wset
-    x = torch.empty((0, 4, 2560), device=dev())
-    out = torch.full((0, 4, 2560), 7.0, device=dev())
-    mean = torch.full((0, 2560), 7.0, device=dev())
-    reader.read(x, out=out, mean=mean)
+    x = to_dev(gen.activations(3, 2))
+    out = torch.full((2, 4, 2560), 7.0, device=dev())
+    mean = torch.full((2, 2560), -3.0, device=dev())
+    reader.scratch.fill_(0xA5)
     torch.cuda.synchronize()
+    rc = hcr.hcr_read(reader.handle, 0, x.data_ptr(), None, None, out.data_ptr(), mean.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream)
+    assert rc == hcr.HCR_OK
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(mean == -3.0) and torch.all(reader.scratch == 0xA5)
+    # the binding's empty read is the same call
+    reader.read(torch.empty((0, 4, 2560), device=dev()), out=torch.empty((0, 4, 2560), device=dev()),
+                mean=torch.empty((0, 2560), device=dev()))
+    torch.cuda.synchronize()
+    assert torch.all(reader.scratch == 0xA5)
 
 
 def test_in_place_out_on_x_and_on_pending(wset):
@@ -249,8 +261,8 @@ def test_single_token_read_agrees_with_windows(wset):
 
 
 def test_numerics_stress_graph_replay_bitwise():
-    """The stress workload's reads captured in one graph: replays equal the direct calls bit for bit."""
-    c = gen.numerics_stress(5, n_sets=8)
+    """The stress workload's 32 reads captured in one graph: replays equal the direct calls bit for bit."""
+    c = gen.numerics_stress(5, n_sets=32)
     readers = [reader_for(w) for w in c["weights"]]
     xs = [to_dev(x) for x in c["x"]]
     ps = [to_dev(p) for p in c["pending"]]
@@ -270,8 +282,9 @@ def test_numerics_stress_graph_replay_bitwise():
                 r.read(xs[k], ps[k], ij[k], out=outs[k], mean=means[k])
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(3):
-        for o in outs:
+        for o, m in zip(outs, means):
             o.fill_(float("nan"))
+            m.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         for k, (o, m) in enumerate(direct):

@@ -199,3 +199,23 @@ def test_q8_residual_chain_of_16_reads():
         ref = s.ref_read(x_host, c["pending"][i])
         check_read(s.reader, T, out, mean, ref, f"Q8_0 chain step {i}")
         x, x_host = out, out.cpu().numpy()
+
+
+def test_quantize_overflowing_block_scale_is_infinite_and_read_is_not_finite():
+    """A block whose largest |w| exceeds 127 * 65504 (the largest finite binary16 times 127) gets d = amax / 127
+    above binary16's range: the stored scale is +inf (as the reference's), and a read on such copies has
+    non-finite outputs.  The header states the bound; the weights of the read here stay far below it."""
+    w = gen.weight_set(13, 0)
+    bits = w.w_down.copy()
+    big = np.float32(2.0e7)  # its BF16 truncation is still far above 127 * 65504 = 8,319,008
+    b16 = (np.array([big], np.float32).view(np.uint32) >> 16).astype(np.uint16)[0]
+    bits[5, 64] = b16  # row 5, block 2
+    codes, scales = _assert_same_copy(bits, "one overflowing block")
+    s = scales.cpu().numpy().view(np.uint16)
+    assert s[5, 2] == 0x7C00, hex(int(s[5, 2]))          # +inf in binary16
+    assert np.all(s[5, :2] != 0x7C00) and np.all(s[4] != 0x7C00)
+    uc, us = _quantize_on_gpu(w.w_up)
+    reader = hcr.HCRead.q8_0(codes, scales, uc, us, to_dev(w.w_norm))
+    out, mean = reader.read(to_dev(gen.activations(13, 2)))
+    torch.cuda.synchronize()
+    assert not torch.isfinite(out).all() and not torch.isfinite(mean).all()

@@ -66,8 +66,9 @@ def test_window_steps_and_graph_replay(window):
             _chain(readers, pend, x0, outs, means)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(3):
-        for o in outs:
+        for o, m in zip(outs, means):
             o.fill_(float("nan"))
+            m.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         for i in range(N_READS):
