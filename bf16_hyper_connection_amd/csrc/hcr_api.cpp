@@ -123,10 +123,14 @@ int hcr_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, fl
   return hcr::launch_matvec_bf16(w, rows, cols, T, x, y, stream);
 }
 
-int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj, float* out, float* mean,
-             void* stream) {
-  if (!h || T < 0 || T > hcr::TMAX) return HCR_EINVAL;
-  if (T == 0) return HCR_OK;
+}  // extern "C"
+
+namespace {
+
+// The argument checks of a read on h's weights (h.scratch null: the library's own scratch, which no caller
+// buffer can overlap); HCR_OK when the read may be enqueued.
+int check_read(const hcr_handle* h, int T, const float* x, const float* pending, const float* inj, float* out,
+               float* mean) {
   if (!x || !out || !mean) return HCR_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(mean, 16) || (pending && !aligned(pending, 16)) ||
       (inj && !aligned(inj, 16)))
@@ -150,9 +154,37 @@ int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* 
   if (overlap(sc, sx) || overlap(sc, sp) || overlap(sc, si)) return HCR_EALIAS;
   for (const Span& w : sw)
     if (overlap(so, w) || overlap(sm, w)) return HCR_EALIAS;
+  return HCR_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj, float* out, float* mean,
+             void* stream) {
+  if (!h || T < 0 || T > hcr::TMAX) return HCR_EINVAL;
+  if (T == 0) return HCR_OK;
+  const int rc = check_read(h, T, x, pending, inj, out, mean);
+  if (rc != HCR_OK) return rc;
   return hcr::launch_read(h->fmt, T, h->w_down, h->s_down, h->w_up, h->s_up, h->w_norm, h->scratch, x, pending, inj,
                           out, mean, stream);
+}
+
+int hcr_read_static(const void* w_down, const void* w_up, const float* w_norm, int T, const float* x,
+                    const float* pending, const float* inj, float* out, float* mean, void* stream) {
+  if (T < 0 || T > hcr::TMAX) return HCR_EINVAL;
+  if (T == 0) return HCR_OK;
+  if (!w_down || !w_up || !w_norm) return HCR_EINVAL;
+  if (!aligned(w_down, 16) || !aligned(w_up, 16) || !aligned(w_norm, 16)) return HCR_EALIGN;
+  const hcr_handle h{hcr::FMT_BF16, w_down, w_up, nullptr, nullptr, w_norm, nullptr};
+  int rc = check_read(&h, T, x, pending, inj, out, mean);
+  if (rc != HCR_OK) return rc;
+  void* sc = nullptr;
+  rc = hcr::static_scratch(stream, &sc);
+  if (rc != HCR_OK) return rc;
+  return hcr::launch_read(hcr::FMT_BF16, T, w_down, nullptr, w_up, nullptr, w_norm, sc, x, pending, inj, out, mean,
+                          stream);
 }
 
 void hcr_destroy(hcr_t h) { free(h); }

@@ -93,6 +93,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "hcr_device.h"
 #include "hcr_layout.h"
 
@@ -814,6 +817,45 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(mfma ? upm_threads(T) : UP_THREADS), 0, st, w_up, s_up, part, inj,
                      pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// the library's own scratch (hcr_read_static): one array per GPU, held until the process ends
+// ---------------------------------------------------------------------------
+// In host code `scratch` names a host-side stand-in, not a device address: the kernels get the address
+// hipGetSymbolAddress gives for the device the read runs on, found once per device with that device
+// current.  Every call on one GPU shares its array, so calls that overlap in time on one GPU race (the
+// caller orders them, e.g. on one stream).  Nothing in it needs to start at zero: each read writes every
+// partial, lo and rs value before reading it.
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+}  // namespace
+
+int static_scratch(void* stream, void** out) {
+  *out = nullptr;
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return HCR_EHIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev) != hipSuccess) return HCR_EHIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return HCR_EHIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (dev != cur && hipSetDevice(dev) != hipSuccess) return HCR_EHIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur && hipSetDevice(cur) != hipSuccess) return HCR_EHIP;
+      if (e != hipSuccess || !p) return HCR_EHIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return HCR_OK;
 }
 
 }  // namespace hcr

@@ -108,6 +108,10 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
                 const float* w_norm, void* scratch, const float* x, const float* pending, const float* inj,
                 float* out, float* mean, void* stream);
 
+// The device address of the library's own scratch (SCRATCH_BYTES, 256-byte aligned) on the device of
+// `stream` (the current device for the null stream), found once per device; HCR_OK or HCR_EHIP.
+int static_scratch(void* stream, void** out);
+
 // ---- skinny BF16 matvec: a wave takes one group of MV_ROWS_PER_WAVE rows
 constexpr int MV_THREADS = 256;
 constexpr int MV_ROWS_PER_WAVE = 4;

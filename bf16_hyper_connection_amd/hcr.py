@@ -49,6 +49,8 @@ def lib():
         L.hcr_matvec_bf16.argtypes = [vp, ip, ip, ip, vp, vp, vp]
         L.hcr_read.restype = ip
         L.hcr_read.argtypes = [vp, ip, vp, vp, vp, vp, vp, vp]
+        L.hcr_read_static.restype = ip
+        L.hcr_read_static.argtypes = [vp, vp, vp, ip, vp, vp, vp, vp, vp, vp]
         L.hcr_destroy.restype = None
         L.hcr_destroy.argtypes = [vp]
         L.hcr_strerror.restype = ctypes.c_char_p
@@ -157,6 +159,13 @@ def matvec_bf16(w, x, y=None, stream=None):
 def hcr_read(h, T, x, pending, inj, out, mean, stream):
     """Raw-pointer form (ints or None); returns the status code without raising."""
     return lib().hcr_read(_raw(h), int(T), _raw(x), _raw(pending), _raw(inj), _raw(out), _raw(mean), _raw(stream))
+
+
+def hcr_read_static(w_down, w_up, w_norm, T, x, pending, inj, out, mean, stream):
+    """Raw-pointer form (ints or None) of the read on the library's own scratch; returns the status code
+    without raising."""
+    return lib().hcr_read_static(_raw(w_down), _raw(w_up), _raw(w_norm), int(T), _raw(x), _raw(pending), _raw(inj),
+                                 _raw(out), _raw(mean), _raw(stream))
 
 
 def hcr_destroy(h):

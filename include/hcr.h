@@ -148,6 +148,26 @@ int hcr_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, fl
 int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* inj,
              float* out, float* mean, void* stream);
 
+/* The read of hcr_read on BF16 weights, for callers that cannot allocate device
+ * memory or keep a scratch buffer per weight set (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): no handle and no
+ * caller scratch.  The partial sums, lo and rs live in the library's own device
+ * array of hcr_scratch_bytes() bytes, one per GPU, held from the first call on
+ * that GPU until the process ends; the first call on a GPU looks its address up
+ * (hipGetSymbolAddress), later calls make no allocation, free or memset.
+ * Every call on one GPU shares that GPU's array: calls whose kernels overlap in
+ * time on one GPU race, so order them (e.g. on one stream).  The read runs on
+ * the device of `stream` (the current device for NULL).
+ *   w_down, w_up, w_norm : as hcr_create (BF16 weights, device pointers, 16-byte aligned)
+ *   T, x, pending, inj, out, mean, stream : as hcr_read
+ * T may be 0..HCR_T_MAX (the array holds HCR_T_MAX tokens; larger T is rejected).
+ * Results are bitwise those of hcr_read on a handle of the same weights.
+ * Errors: HCR_EINVAL (T out of range, a NULL weight, x, out or mean),
+ * HCR_EALIGN, HCR_EALIAS (all before any HIP call), HCR_EHIP (the address
+ * lookup or a launch failed). */
+int hcr_read_static(const void* w_down, const void* w_up, const float* w_norm, int T, const float* x,
+                    const float* pending, const float* inj, float* out, float* mean, void* stream);
+
 /* Free the host-side handle (never the caller's device memory).  NULL is a no-op. */
 void hcr_destroy(hcr_t h);
 

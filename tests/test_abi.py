@@ -200,3 +200,30 @@ def test_source_hash_ignores_comments_only():
     assert a == b
     assert build._code_only('const char* s = "// not a comment";') == 'const char* s = "// not a comment";'
     assert build._code_only("int a = 1;") != build._code_only("int a = 2;")
+
+
+# ---- the read on the library's own scratch (rejections only: a valid call would launch kernels)
+@pytest.mark.parametrize("T,kw,rc", [
+    (17, {}, hcr.HCR_EINVAL),
+    (-1, {}, hcr.HCR_EINVAL),
+    (2, dict(w_down=None), hcr.HCR_EINVAL),
+    (2, dict(w_norm=None), hcr.HCR_EINVAL),
+    (2, dict(x=None), hcr.HCR_EINVAL),
+    (2, dict(mean=None), hcr.HCR_EINVAL),
+    (2, dict(w_up=WU + 8), hcr.HCR_EALIGN),
+    (2, dict(x=X + 4), hcr.HCR_EALIGN),
+    (2, dict(out=X + 16), hcr.HCR_EALIAS),      # partial overlap with x
+    (2, dict(mean=O + 64), hcr.HCR_EALIAS),     # mean inside out
+    (2, dict(out=WD + MB), hcr.HCR_EALIAS),     # out on the weights
+    (2, dict(mean=WN), hcr.HCR_EALIAS),         # mean on w_norm
+])
+def test_read_static_rejects_before_any_hip_call(lib, T, kw, rc):
+    a = dict(w_down=WD, w_up=WU, w_norm=WN, x=X, pending=P, inj=I, out=O, mean=M)
+    a.update(kw)
+    got = hcr.hcr_read_static(a["w_down"], a["w_up"], a["w_norm"], T, a["x"], a["pending"], a["inj"], a["out"],
+                              a["mean"], None)
+    assert got == rc, (got, hcr.hcr_strerror(got))
+
+
+def test_read_static_empty_is_noop(lib):
+    assert hcr.hcr_read_static(None, None, None, 0, None, None, None, None, None, None) == hcr.HCR_OK
