@@ -12,7 +12,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhcr.so")
+# HCR_LIB names another build of the same C ABI (the tests run the host-sanitizer build through it)
+LIB_PATH = os.environ.get("HCR_LIB") or os.path.join(_PKG, "libhcr.so")
 
 HCR_OK, HCR_EINVAL, HCR_EALIGN, HCR_ESCRATCH, HCR_EALIAS, HCR_EHIP = 0, -1, -2, -3, -4, -5
 

@@ -67,18 +67,28 @@ enum {
 
 typedef struct hcr_handle* hcr_t;
 
-/* Bytes of device scratch one handle needs (partial sums, sums of squares, lo, rs). */
+/* Bytes of device scratch one handle needs (partial sums, sums of squares, lo, rs).
+ * Basis: Strata PR #2812, Title (the two-kernel read reuses the argument struct,
+ * scratch and helpers of the Q8_0 read it builds on); What changed (the down
+ * kernel's partial sums and the lo / injection / rs it writes live there). */
 size_t hcr_scratch_bytes(void);
 
 /* Byte offsets, inside a handle's scratch, of the last read's lo (float [T][320])
- * and rs (float [T][4]); valid after the read's kernels complete. */
+ * and rs (float [T][4]); valid after the read's kernels complete.  Basis: Strata
+ * PR #2812, What changed (the finish writes lo / the injection and rs) and Summary
+ * (lo / rs / mixed are the outputs compared with the default read). */
 int hcr_scratch_layout(size_t* lo_offset, size_t* rs_offset);
 
-/* Geometry compiled into the library (any argument may be NULL). */
+/* Geometry compiled into the library (any argument may be NULL).  Basis: Strata
+ * PR #2812, What changed (a 1,280-column slab is half a stream; 16 columns x 4
+ * streams per up work-group; K = 320); larger T serve Strata PR #2070's larger
+ * windows (first comment). */
 int hcr_geometry(int* streams, int* stream_d, int* rank, int* t_max);
 
 /* Create a handle for one weight set (one layer half: w_down, w_up, w_norm) and
- * its scratch.  Host-only: records pointers, makes no HIP call.  The weights and
+ * its scratch.  Basis: Strata PR #2812, Title (the argument struct and scratch the
+ * read keeps per layer half) and Summary (same BF16 weights, no extra VRAM).
+ * Host-only: records pointers, makes no HIP call.  The weights and
  * the scratch must stay valid until hcr_destroy.  Errors: HCR_EINVAL (a NULL
  * pointer), HCR_EALIGN, HCR_ESCRATCH, HCR_EALIAS (scratch overlaps a weight). */
 int hcr_create(const void* w_down, const void* w_up, const float* w_norm,
@@ -133,7 +143,10 @@ int hcr_create_q8_0(const void* down_codes, const void* down_scales, const void*
 int hcr_matvec_bf16(const void* w, int rows, int cols, int T, const float* x, float* y, void* stream);
 
 /* One HC read of T tokens, asynchronous on `stream` (a hipStream_t; NULL is the
- * null stream).  Enqueues two kernels and returns; no host synchronisation,
+ * null stream).  Basis: Strata PR #2812, Summary (the norm, the down projection
+ * and its partial reduction in one kernel, the up projection in a second) and
+ * What changed (the up kernel's epilogue: pending write, gate, stream mean).
+ * Enqueues two kernels and returns; no host synchronisation,
  * allocation or memset, so it can be captured into a HIP graph.
  *   x        [T][4][2560]  read only
  *   pending  [T][4][2560]  or NULL (no pending write)
@@ -168,10 +181,15 @@ int hcr_read(hcr_t h, int T, const float* x, const float* pending, const float* 
 int hcr_read_static(const void* w_down, const void* w_up, const float* w_norm, int T, const float* x,
                     const float* pending, const float* inj, float* out, float* mean, void* stream);
 
-/* Free the host-side handle (never the caller's device memory).  NULL is a no-op. */
+/* Free the host-side handle (never the caller's device memory).  NULL is a no-op.
+ * Basis: Strata PR #2812, Title (the handle is the read's argument struct; the
+ * weights and the scratch stay the caller's). */
 void hcr_destroy(hcr_t h);
 
-/* Static text naming an error code. */
+/* Static text naming an error code.  Basis: Strata PR #2812, What changed
+ * (arguments not at the callers' fixed strides fall back to the default read
+ * with one line on stderr; this library has one code path, so such a call
+ * returns an error code, and this is its line of text). */
 const char* hcr_strerror(int rc);
 
 #ifdef __cplusplus
