@@ -153,16 +153,36 @@ def ab_compare(args, readers, xs, outs, means, stream, timed):
         L.hcr_scratch_bytes.restype, L.hcr_scratch_bytes.argtypes = ctypes.c_size_t, []
         L.hcr_create.restype, L.hcr_create.argtypes = ctypes.c_int, [vp, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
         L.hcr_read.restype, L.hcr_read.argtypes = ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+        L.hcr_quantize_q8_0.restype = ctypes.c_int
+        L.hcr_quantize_q8_0.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.hcr_create_q8_0.restype = ctypes.c_int
+        L.hcr_create_q8_0.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
         nb = L.hcr_scratch_bytes()
-        handles, scratch = [], []
+        handles, scratch = [], []  # scratch: every device buffer a handle needs alive
         for r in readers:
-            sc = torch.empty(nb, dtype=torch.uint8, device=r.w_down.device)
+            dev = r.w_down.device
+            sc = torch.empty(nb, dtype=torch.uint8, device=dev)
             h = vp()
-            rc = L.hcr_create(r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(), sc.data_ptr(), nb,
-                              ctypes.byref(h))
+            if args.ab_q8:
+                bufs = []
+                for w in (r.w_down, r.w_up):
+                    rows, cols = w.shape
+                    c = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+                    sg = torch.empty((rows, cols // 32), dtype=torch.int16, device=dev)
+                    rc = L.hcr_quantize_q8_0(w.data_ptr(), rows, cols, c.data_ptr(), sg.data_ptr(),
+                                             vp(torch.cuda.current_stream().cuda_stream))
+                    assert rc == 0, (path, rc)
+                    bufs += [c, sg]
+                rc = L.hcr_create_q8_0(bufs[0].data_ptr(), bufs[1].data_ptr(), bufs[2].data_ptr(), bufs[3].data_ptr(),
+                                       r.w_norm.data_ptr(), sc.data_ptr(), nb, ctypes.byref(h))
+                scratch.append((sc, bufs))
+            else:
+                rc = L.hcr_create(r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(), sc.data_ptr(), nb,
+                                  ctypes.byref(h))
+                scratch.append(sc)
             assert rc == 0, (path, rc)
             handles.append(h)
-            scratch.append(sc)
+        torch.cuda.synchronize()
         graphs = {}
         for T in Ts:
             g = torch.cuda.CUDAGraph()
@@ -200,6 +220,7 @@ def sha256_of(*tensors):
 
 
 def main():
+    import ctypes
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -217,6 +238,7 @@ def main():
                          "(alternating, --ab-rounds rounds), print one JSON line of the comparison and exit")
     ap.add_argument("--ab-rounds", type=int, default=3)
     ap.add_argument("--ab-tmax", type=int, default=8, help="A/B mode: T = 1..this")
+    ap.add_argument("--ab-q8", action="store_true", help="A/B mode: read Q8_0 copies (each build quantises)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -350,10 +372,30 @@ def main():
             log(f"bench: calibration {key}: {calibration[key]}")
         calibration["read_over_loads_us"] = {T: round(per_T_us[T] - calibration["loads_pair_us"][T], 3)
                                              for T in range(1, T_WIDE + 1)}
+        # the two up kernels alone, per T (graphs of 32, each on a set's W_up and scratch): the read dispatches
+        # the vector-ALU one at T = 1 and the matrix-core one from T = 2
+        cal.hcrc_up_kernel.restype = ctypes.c_int
+        cal.hcrc_up_kernel.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
+        for kind, key in ((0, "up_valu_us"), (1, "up_mfma_us")):
+            calibration[key] = {}
+            for T in range(1, T_WIDE + 1):
+                gk = torch.cuda.CUDAGraph()
+                stream.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(stream):
+                    with torch.cuda.graph(gk, stream=stream):
+                        for r in readers:
+                            rc = cal.hcrc_up_kernel(kind, T, r.w_up.data_ptr(), r.scratch.data_ptr(),
+                                                    outs[T].data_ptr(), means[T].data_ptr(), stream.cuda_stream)
+                            assert rc == hcr.HCR_OK, rc
+                torch.cuda.current_stream().wait_stream(stream)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                del gk
+            log(f"bench: calibration {key}: {calibration[key]}")
         calibration["note"] = ("per T, graphs of 32 pairs on the read's grids and work-group sizes over the 32 rotated "
                                "weight sets, replayed like the per-T figures: empty_pair = two empty kernels, "
                                "loads_pair = the read's global loads only (same order, widths and cache policy; no "
-                               "arithmetic, LDS, barrier or store); read_over_loads = per_T_us - loads_pair")
+                               "arithmetic, LDS, barrier or store); read_over_loads = per_T_us - loads_pair; "
+                               "up_valu / up_mfma = the read's two up kernels alone, µs per launch")
 
     # the full epilogue (pending write and injection on) over the same 32 rotated weight sets: T = 4 with the
     # seeded x, pending and injection of the full-epilogue workload, and T = 8 with those of the numerics-stress

@@ -14,6 +14,7 @@
 #include "hcr_calib.h"
 #include "hcr_device.h"
 #include "hcr_layout.h"
+#include "hcr_up.h"
 
 namespace hcr {
 namespace {
@@ -189,6 +190,34 @@ static_assert(UP_MFMA_FROM == 2, "the read dispatches hc_up at T = 1 and hc_up_m
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
+typedef void (*up_fn)(const void*, const uint16_t*, const float*, const float*, const float*, float*, float*,
+                      float*);
+// the read's two up kernels under names of their own (the same bodies, BF16 weights, no pending write or
+// injection), so that a kernel trace tells them from the read's dispatches
+template <int T>
+__global__ __launch_bounds__(UP_THREADS) void cal_up_valu(const void* w_up, const uint16_t* s_up, const float* part,
+                                                          const float* inj, const float* pending, float* out,
+                                                          float* mean, float* lo_out) {
+  hc_up_body<T, false, false, FMT_BF16>(w_up, s_up, part, inj, pending, out, mean, lo_out);
+}
+template <int T>
+__global__ __launch_bounds__(256) void cal_up_mfma(const void* w_up, const uint16_t* s_up, const float* part,
+                                                   const float* inj, const float* pending, float* out, float* mean,
+                                                   float* lo_out) {
+  hc_up_mfma_body<T, false, false, FMT_BF16>(w_up, s_up, part, inj, pending, out, mean, lo_out);
+}
+#define HCRC_UP_T(K, T) K<T>
+const up_fn kUpValu[TMAX] = {HCRC_UP_T(cal_up_valu, 1),  HCRC_UP_T(cal_up_valu, 2),  HCRC_UP_T(cal_up_valu, 3),  HCRC_UP_T(cal_up_valu, 4),
+                             HCRC_UP_T(cal_up_valu, 5),  HCRC_UP_T(cal_up_valu, 6),  HCRC_UP_T(cal_up_valu, 7),  HCRC_UP_T(cal_up_valu, 8),
+                             HCRC_UP_T(cal_up_valu, 9),  HCRC_UP_T(cal_up_valu, 10), HCRC_UP_T(cal_up_valu, 11), HCRC_UP_T(cal_up_valu, 12),
+                             HCRC_UP_T(cal_up_valu, 13), HCRC_UP_T(cal_up_valu, 14), HCRC_UP_T(cal_up_valu, 15), HCRC_UP_T(cal_up_valu, 16)};
+const up_fn kUpMfma[TMAX] = {
+    HCRC_UP_T(cal_up_mfma, 1),  HCRC_UP_T(cal_up_mfma, 2),  HCRC_UP_T(cal_up_mfma, 3),  HCRC_UP_T(cal_up_mfma, 4),
+    HCRC_UP_T(cal_up_mfma, 5),  HCRC_UP_T(cal_up_mfma, 6),  HCRC_UP_T(cal_up_mfma, 7),  HCRC_UP_T(cal_up_mfma, 8),
+    HCRC_UP_T(cal_up_mfma, 9),  HCRC_UP_T(cal_up_mfma, 10), HCRC_UP_T(cal_up_mfma, 11), HCRC_UP_T(cal_up_mfma, 12),
+    HCRC_UP_T(cal_up_mfma, 13), HCRC_UP_T(cal_up_mfma, 14), HCRC_UP_T(cal_up_mfma, 15), HCRC_UP_T(cal_up_mfma, 16)};
+#undef HCRC_UP_T
+
 }  // namespace
 }  // namespace hcr
 
@@ -215,5 +244,24 @@ extern "C" int hcrc_read_floor(int kind, int T, const void* w_down, const void* 
     hipLaunchKernelGGL(kCalUp[T - 1], dim3(UP_WGS), dim3(up_threads), 0, st, static_cast<const uint16_t*>(w_up),
                        part);
   }
+  return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}
+
+extern "C" int hcrc_up_kernel(int kind, int T, const void* w_up, void* scratch, float* out, float* mean,
+                              void* stream) {
+  using namespace hcr;
+  if ((kind != HCRC_UP_VALU && kind != HCRC_UP_MFMA) || T < 1 || T > TMAX) return HCR_EINVAL;
+  if (!w_up || !scratch || !out || !mean) return HCR_EINVAL;
+  if (!aligned(w_up, 16) || !aligned(scratch, 256) || !aligned(out, 16) || !aligned(mean, 16)) return HCR_EALIGN;
+  char* sc = static_cast<char*>(scratch);
+  const float* part = reinterpret_cast<const float*>(sc + OFF_PART);
+  float* lo = reinterpret_cast<float*>(sc + OFF_LO);
+  (void)hipGetLastError();
+  if (kind == HCRC_UP_VALU)
+    hipLaunchKernelGGL(kUpValu[T - 1], dim3(UP_WGS), dim3(UP_THREADS), 0, reinterpret_cast<hipStream_t>(stream), w_up,
+                       nullptr, part, nullptr, nullptr, out, mean, lo);
+  else
+    hipLaunchKernelGGL(kUpMfma[T - 1], dim3(UP_WGS), dim3(upm_threads(T)), 0, reinterpret_cast<hipStream_t>(stream),
+                       w_up, nullptr, part, nullptr, nullptr, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }

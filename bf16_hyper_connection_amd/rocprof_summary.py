@@ -51,6 +51,20 @@ def kernel_key(name):
     m = re.search(r"hcr::mv_bf16<(\d+), (\d+)>", name)
     if m:
         return ("matvec", int(m.group(1)), int(m.group(2)))
+    # the calibration library (include/hcr_calib.h)
+    if "cal_empty" in name:
+        return ("cal_empty",)
+    m = re.search(r"cal_down_loads<(\d+)>", name)
+    if m:
+        return ("cal_down_loads", int(m.group(1)))
+    if "cal_up1_loads" in name:
+        return ("cal_up_loads", 1)
+    m = re.search(r"cal_up_mfma_loads<(\d+)>", name)
+    if m:
+        return ("cal_up_loads", int(m.group(1)))
+    m = re.search(r"cal_up_(valu|mfma)<(\d+)>", name)
+    if m:
+        return ("cal_up_" + m.group(1), int(m.group(2)))
     return None
 
 
@@ -288,6 +302,33 @@ def main():
             for T, v in sorted(tr[5].items()):
                 p10, p50, p90 = percentiles(v)
                 md.append(f"| {T} | {len(v)} | {p10:.3f} | {p50:.3f} | {p90:.3f} |")
+    cal_lines, ab_lines = [], []
+    for T in range(1, 17):
+        kd, ku, kld, klu = ("down", T, 0, False, False), ("up", T, 0, False, False), ("cal_down_loads", T), \
+            ("cal_up_loads", T)
+        if kld in dur and klu in dur and kd in dur and ku in dur:
+            cal_lines.append(f"| {T} | {dur[kd][0]:.3f} | {dur[kld][0]:.3f} | {dur[kd][0] - dur[kld][0]:+.3f} | "
+                             f"{dur[ku][0]:.3f} | {dur[klu][0]:.3f} | {dur[ku][0] - dur[klu][0]:+.3f} |")
+        kv, km = ("cal_up_valu", T), ("cal_up_mfma", T)
+        if kv in dur and km in dur:
+            rec.setdefault("up_kernels_alone", {})[str(T)] = {"valu_us": round(dur[kv][0], 3),
+                                                             "mfma_us": round(dur[km][0], 3)}
+            ab_lines.append(f"| {T} | {dur[kv][0]:.3f} | {dur[km][0]:.3f} | {dur[km][0] - dur[kv][0]:+.3f} | "
+                            f"{'matrix cores' if T >= 2 else 'vector ALUs'} |")
+    if ("cal_empty",) in dur:
+        rec["cal_empty_avg_us"] = round(dur[("cal_empty",)][0], 3)
+    if cal_lines:
+        md += ["", "Calibration kernels (`libhcr_calib.so`, the read's grids with only its global loads) against the "
+                   "read's own kernels, BF16, average µs per dispatch"
+                   + (f"; an empty kernel on the same grids averages {dur[('cal_empty',)][0]:.3f} µs"
+                      if ("cal_empty",) in dur else "") + ":", "",
+               "| T | hc_down | its loads alone | excess | up kernel | its loads alone | excess |",
+               "|---|---|---|---|---|---|---|"] + cal_lines
+    if ab_lines:
+        md += ["", "The two up kernels alone (the calibration library's `cal_up_valu<T>` = hc_up's body, "
+                   "`cal_up_mfma<T>` = hc_up_mfma's body; BF16, no pending write or injection), average µs per "
+                   "dispatch:", "", "| T | vector ALUs (v_dot2) | matrix cores | difference | the read dispatches |",
+               "|---|---|---|---|---|"] + ab_lines
     if q in dur:
         md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
                    f"{dur[q][1]} calls."]

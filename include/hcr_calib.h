@@ -44,6 +44,27 @@ enum { HCRC_EMPTY = 0, HCRC_LOADS = 1 };
 int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
                     const void* scratch, const float* x, void* stream);
 
+/*
+ * hcrc_up_kernel: enqueue one of the read's two up-projection kernels alone, for
+ * T tokens (1..HCR_T_MAX), BF16 weights, no pending write or injection, so that
+ * the two can be timed against each other at every T (the read dispatches the
+ * vector-ALU kernel at T = 1 and the matrix-core kernel from T = 2; Strata PR
+ * #2812's up kernel is the basis of both, What changed):
+ *   HCRC_UP_VALU  hc_up (v_dot2_f32_bf16 on lo split into BF16 high and low parts)
+ *   HCRC_UP_MFMA  hc_up_mfma (v_mfma_f32_16x16x32_bf16, the same split)
+ * w_up: BF16 [10240][320]; scratch: a handle's scratch (hcr_scratch_bytes()
+ * bytes, 256-byte aligned), whose stream partials are read as the up kernel
+ * reads them after a down kernel and whose lo slot is written; out float
+ * [T][4][2560] and mean float [T][2560] are written.  All device pointers,
+ * 16-byte aligned, none overlapping.  The values computed are those of a read
+ * whose down kernel left the scratch's partials; the call is for timing.
+ * Errors: HCR_EINVAL (unknown kind, T out of range, a NULL pointer), HCR_EALIGN
+ * (both before any HIP call), HCR_EHIP.
+ */
+enum { HCRC_UP_VALU = 0, HCRC_UP_MFMA = 1 };
+
+int hcrc_up_kernel(int kind, int T, const void* w_up, void* scratch, float* out, float* mean, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,13 +23,15 @@ def cal():
     vp = ctypes.c_void_p
     L.hcrc_read_floor.restype = ctypes.c_int
     L.hcrc_read_floor.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    L.hcrc_up_kernel.restype = ctypes.c_int
+    L.hcrc_up_kernel.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
     return L
 
 
 def test_exports_every_declared_symbol(cal):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(hcrc_[a-z_]+)\s*\(", text)))
-    assert names == ["hcrc_read_floor"]
+    assert names == ["hcrc_read_floor", "hcrc_up_kernel"]
     for n in names:
         assert hasattr(cal, n)
 
@@ -78,3 +80,52 @@ def test_pairs_run_and_write_nothing(cal, T):
     for a, b in zip(snap, (r.w_down, r.w_up, r.w_norm, r.scratch, x)):
         assert torch.equal(a, b)
     assert np.isfinite(x.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("kind,T,kw,rc", [
+    (2, 1, {}, HCR_EINVAL),
+    (0, 0, {}, HCR_EINVAL),
+    (1, 17, {}, HCR_EINVAL),
+    (1, 2, dict(out=None), HCR_EINVAL),
+    (0, 2, dict(sc=None), HCR_EINVAL),
+    (1, 2, dict(sc=0x40000040), HCR_EALIGN),
+    (0, 2, dict(mean=0x70000004), HCR_EALIGN),
+])
+def test_up_kernel_rejects_before_any_hip_call(cal, kind, T, kw, rc):
+    a = dict(wu=0x20000000, sc=0x40000000, out=0x60000000, mean=0x70000000)
+    a.update(kw)
+    assert cal.hcrc_up_kernel(kind, T, a["wu"], a["sc"], a["out"], a["mean"], None) == rc
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 12])
+def test_up_kernels_alone_reproduce_the_read(cal, T):
+    """After a read, either up kernel run alone on the handle's scratch gives the read's out and mean: bitwise
+    for the one the read dispatches at T, within 1e-5 of max |out| for the other."""
+    import torch
+
+    from bf16_hyper_connection_amd import hcr
+    from bf16_hyper_connection_amd import inputs as gen
+    from tests.gpu_util import dev, reader_for, to_dev
+
+    print(f"up kernels alone T={T}", flush=True)
+    r = reader_for(gen.weight_set(0, 1))
+    x = to_dev(gen.activations(1, T))
+    ref_o, ref_m = r.read(x)
+    torch.cuda.synchronize()
+    ref_o, ref_m = ref_o.clone(), ref_m.clone()
+    st = torch.cuda.current_stream().cuda_stream
+    got = {}
+    for kind in (0, 1):
+        o = torch.full((T, 4, 2560), float("nan"), device=dev())
+        m = torch.full((T, 2560), float("nan"), device=dev())
+        rc = cal.hcrc_up_kernel(kind, T, r.w_up.data_ptr(), r.scratch.data_ptr(), o.data_ptr(), m.data_ptr(), st)
+        assert rc == HCR_OK, hcr.hcr_strerror(rc)
+        torch.cuda.synchronize()
+        got[kind] = (o, m)
+    dispatched = 0 if T == 1 else 1
+    assert torch.equal(got[dispatched][0], ref_o) and torch.equal(got[dispatched][1], ref_m)
+    scale = float(ref_o.abs().max())
+    other = got[1 - dispatched]
+    assert float((other[0] - ref_o).abs().max()) <= 1e-5 * scale
+    assert float((other[1] - ref_m).abs().max()) <= 1e-5 * scale
