@@ -354,8 +354,8 @@ def main():
     calibration = None
     if not args.no_calibration:
         cal = calib_lib()
-        calibration = {"empty_pair_us": {}, "loads_pair_us": {}}
-        for kind, key in ((0, "empty_pair_us"), (1, "loads_pair_us")):
+        calibration = {"empty_pair_us": {}, "loads_pair_us": {}, "loads_store_pair_us": {}}
+        for kind, key in ((0, "empty_pair_us"), (1, "loads_pair_us"), (2, "loads_store_pair_us")):
             for T in range(1, T_WIDE + 1):
                 gk = torch.cuda.CUDAGraph()
                 stream.wait_stream(torch.cuda.current_stream())
@@ -370,6 +370,28 @@ def main():
                 calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
                 del gk
             log(f"bench: calibration {key}: {calibration[key]}")
+        # the pages' down shape (10 rows x a 1,280-column slab) and its last-arriver finish, as load / store /
+        # finish probes (include/hcr_calib.h, hcrc_slab_pair), T = 1..8, one zero-filled slab scratch
+        cal.hcrc_slab_pair.restype = ctypes.c_int
+        cal.hcrc_slab_pair.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
+        slab_sc = torch.zeros(256 * 1024, dtype=torch.uint8, device=dev)
+        for kind, key in ((0, "slab_loads_pair_us"), (1, "slab_stores_pair_us"), (2, "slab_finish_pair_us")):
+            calibration[key] = {}
+            for T in range(1, TMAX + 1):
+                gk = torch.cuda.CUDAGraph()
+                stream.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(stream):
+                    with torch.cuda.graph(gk, stream=stream):
+                        for r in readers:
+                            rc = cal.hcrc_slab_pair(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(),
+                                                    r.w_norm.data_ptr(), slab_sc.data_ptr(), xs[T].data_ptr(),
+                                                    stream.cuda_stream)
+                            assert rc == hcr.HCR_OK, rc
+                torch.cuda.current_stream().wait_stream(stream)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                del gk
+            log(f"bench: calibration {key}: {calibration[key]}")
+        del slab_sc
         calibration["read_over_loads_us"] = {T: round(per_T_us[T] - calibration["loads_pair_us"][T], 3)
                                              for T in range(1, T_WIDE + 1)}
         # the two up kernels alone, per T (graphs of 32, each on a set's W_up and scratch): the read dispatches
@@ -394,7 +416,10 @@ def main():
         calibration["note"] = ("per T, graphs of 32 pairs on the read's grids and work-group sizes over the 32 rotated "
                                "weight sets, replayed like the per-T figures: empty_pair = two empty kernels, "
                                "loads_pair = the read's global loads only (same order, widths and cache policy; no "
-                               "arithmetic, LDS, barrier or store); read_over_loads = per_T_us - loads_pair; "
+                               "arithmetic, LDS, barrier or store); loads_store_pair = loads_pair with one store per down "
+                               "work-group; read_over_loads = per_T_us - loads_pair; slab_* = the pages' 10-row x "
+                               "1,280-column down shape: its loads (up kernel loading lo only), + its partial stores, "
+                               "+ the last-arriver finish (agent-scope acquire-release counter); "
                                "up_valu / up_mfma = the read's two up kernels alone, µs per launch")
 
     # the full epilogue (pending write and injection on) over the same 32 rotated weight sets: T = 4 with the

@@ -53,12 +53,14 @@ struct ColsRaw {
   }
 };
 
-template <int T>
+template <int T, bool STORE>
 __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t* __restrict__ w_down,
                                                                   const float* __restrict__ x,
-                                                                  const float* __restrict__ w_norm) {
+                                                                  const float* __restrict__ w_norm,
+                                                                  float* __restrict__ dst) {
   const int s = down_stream(blockIdx.x), g = down_group(blockIdx.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (STORE && tid == 0) dst[blockIdx.x] = 1.0f;  // one store per work-group, before the loads
   constexpr int WAVES = down_waves(T), CA = down_ca(T), CB = down_cb(T);
   const int ca = (2048 / WAVES) * wave + CA * lane;
   const int cb = 2048 + (512 / WAVES) * wave + CB * lane;
@@ -173,13 +175,125 @@ __global__ __launch_bounds__(UP_THREADS) void cal_up1_loads(const uint16_t* __re
   for (int m = 0; m < UP_ITERS; ++m) use(wa[m]), use(wb[m]);
 }
 
-typedef void (*cal_down_fn)(const uint16_t*, const float*, const float*);
+
+// ---- the pages' down-kernel shape and finish, as loads (and stores, and the finish) only
+// slab scratch: partials [8 slabs][TMAX][R] at 0, sums of squares [8][TMAX] at SLAB_OFF_SS, counters [32 row
+// groups] at SLAB_OFF_CTR, lo [TMAX][R] at SLAB_OFF_LO
+constexpr int SLABS = 8, SLAB_COLS = DD / SLABS, SLAB_ROWS = 10, SLAB_GROUPS = R / SLAB_ROWS;
+constexpr size_t SLAB_OFF_SS = size_t(SLABS) * TMAX * R * 4;
+constexpr size_t SLAB_OFF_CTR = SLAB_OFF_SS + size_t(SLABS) * TMAX * 4 + 256;
+constexpr size_t SLAB_OFF_LO = SLAB_OFF_CTR + 256;
+static_assert(SLAB_COLS == 1280 && SLABS * SLAB_GROUPS == 256 && SLAB_COLS == 256 * 4 + 256 &&
+                  SLAB_OFF_LO + size_t(TMAX) * R * 4 <= HCRC_SLAB_SCRATCH_BYTES,
+              "8 slabs x 32 row groups of 10 rows; lanes own 4 + 1 columns; the slab scratch holds everything");
+
+template <int T, int KIND>
+__global__ __launch_bounds__(256) void cal_slab_down(const uint16_t* __restrict__ w_down, const float* __restrict__ x,
+                                                     const float* __restrict__ w_norm, char* scratch) {
+  const int b = blockIdx.x;
+  const int sl = (b / XCDS) % SLABS, g = b % XCDS + XCDS * (b / (XCDS * SLABS));  // XCD b % 8 = row group % 8
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ca = sl * SLAB_COLS + 256 * wave + 4 * lane, cb = sl * SLAB_COLS + 1024 + 64 * wave + lane;
+  float* part = reinterpret_cast<float*>(scratch);
+  float* ssb = reinterpret_cast<float*>(scratch + SLAB_OFF_SS);
+  unsigned* ctr = reinterpret_cast<unsigned*>(scratch + SLAB_OFF_CTR);
+  float* lo = reinterpret_cast<float*>(scratch + SLAB_OFF_LO);
+  f32x4 xa[T];
+  float xb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    xa[t] = ld4(x + (size_t)t * DD + ca);
+    xb[t] = x[(size_t)t * DD + cb];
+  }
+  const f32x4 na = ld4(w_norm + ca);
+  const float nb = w_norm[cb];
+  uint2 wa[SLAB_ROWS];
+  uint32_t wb[SLAB_ROWS];
+#pragma unroll
+  for (int r = 0; r < SLAB_ROWS; ++r) {
+    wa[r] = ldw8(w_down + (size_t)(SLAB_ROWS * g + r) * DD + ca);
+    wb[r] = ldw2(w_down + (size_t)(SLAB_ROWS * g + r) * DD + cb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < T; ++t) use(xa[t]), use(xb[t]);
+  use(na), use(nb);
+#pragma unroll
+  for (int r = 0; r < SLAB_ROWS; ++r) use(wa[r]), use(wb[r]);
+  if constexpr (KIND == HCRC_SLAB_LOADS) return;
+  // the work-group's 10 T partials and T sums of squares, one per thread (values arbitrary)
+  if (tid < SLAB_ROWS * T)
+    part[((size_t)sl * TMAX + tid / SLAB_ROWS) * R + SLAB_ROWS * g + tid % SLAB_ROWS] = (float)tid;
+  else if (tid < (SLAB_ROWS + 1) * T)
+    ssb[sl * TMAX + tid - SLAB_ROWS * T] = 1.0f;
+  if constexpr (KIND == HCRC_SLAB_FINISH) {
+    __shared__ int last;
+    __syncthreads();  // every thread's stores precede thread 0's release
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(ctr + g, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = old == SLABS - 1;
+    }
+    __syncthreads();
+    if (last) {  // the 8th work-group of the row group: lo of its 10 rows, then the counter back to zero
+      if (tid < SLAB_ROWS * T) {
+        const int t = tid / SLAB_ROWS, r = SLAB_ROWS * g + tid % SLAB_ROWS;
+        float a = 0.f;
+#pragma unroll
+        for (int q = 0; q < SLABS; ++q) a += part[((size_t)q * TMAX + t) * R + r] * ssb[q * TMAX + t];
+        lo[t * R + r] = a;
+      }
+      if (tid == 0) __hip_atomic_store(ctr + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// the up grid of the read (hc_up_mfma's lanes and W_up tile) loading lo, T x R floats, instead of 4 partials
+template <int T>
+__global__ __launch_bounds__(256) void cal_slab_up(const uint16_t* __restrict__ w_up, const char* scratch) {
+  constexpr int NT = upm_threads(T < 2 ? 2 : T);
+  const float* lo = reinterpret_cast<const float*>(scratch + SLAB_OFF_LO);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c0 = up_tile(blockIdx.x) * UP_COLS;
+  const int li = lane & 15, lg = lane >> 4;
+  const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
+  const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+  constexpr int ITEMS = T * (R / 4);
+  constexpr int NI = (ITEMS + NT - 1) / NT;
+  f32x4 pv[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) pv[n] = ld4(lo + 4 * min(tid + n * NT, ITEMS - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 a[R / 32];
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m) a[m] = ldw16(w_up + j * R + 32 * m + 8 * lg);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NI; ++n) use(pv[n]);
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m) use(a[m]);
+}
+
+typedef void (*slab_down_fn)(const uint16_t*, const float*, const float*, char*);
+typedef void (*slab_up_fn)(const uint16_t*, const char*);
+#define HCRC_SLAB_ROW(K) {cal_slab_down<1, K>, cal_slab_down<2, K>, cal_slab_down<3, K>, cal_slab_down<4, K>, \
+                          cal_slab_down<5, K>, cal_slab_down<6, K>, cal_slab_down<7, K>, cal_slab_down<8, K>}
+const slab_down_fn kSlabDown[3][8] = {HCRC_SLAB_ROW(HCRC_SLAB_LOADS), HCRC_SLAB_ROW(HCRC_SLAB_STORES),
+                                      HCRC_SLAB_ROW(HCRC_SLAB_FINISH)};
+#undef HCRC_SLAB_ROW
+const slab_up_fn kSlabUp[8] = {cal_slab_up<1>, cal_slab_up<2>, cal_slab_up<3>, cal_slab_up<4>,
+                               cal_slab_up<5>, cal_slab_up<6>, cal_slab_up<7>, cal_slab_up<8>};
+
+typedef void (*cal_down_fn)(const uint16_t*, const float*, const float*, float*);
 typedef void (*cal_up_fn)(const uint16_t*, const float*);
 static_assert(TMAX == 16, "the tables below list T = 1..16");
-const cal_down_fn kCalDown[TMAX] = {cal_down_loads<1>,  cal_down_loads<2>,  cal_down_loads<3>,  cal_down_loads<4>,
-                                    cal_down_loads<5>,  cal_down_loads<6>,  cal_down_loads<7>,  cal_down_loads<8>,
-                                    cal_down_loads<9>,  cal_down_loads<10>, cal_down_loads<11>, cal_down_loads<12>,
-                                    cal_down_loads<13>, cal_down_loads<14>, cal_down_loads<15>, cal_down_loads<16>};
+#define HCRC_DOWN_ROW(F)                                                                                       \
+  {cal_down_loads<1, F>,  cal_down_loads<2, F>,  cal_down_loads<3, F>,  cal_down_loads<4, F>,  cal_down_loads<5, F>,  \
+   cal_down_loads<6, F>,  cal_down_loads<7, F>,  cal_down_loads<8, F>,  cal_down_loads<9, F>,  cal_down_loads<10, F>, \
+   cal_down_loads<11, F>, cal_down_loads<12, F>, cal_down_loads<13, F>, cal_down_loads<14, F>, cal_down_loads<15, F>, \
+   cal_down_loads<16, F>}
+const cal_down_fn kCalDown[2][TMAX] = {HCRC_DOWN_ROW(false), HCRC_DOWN_ROW(true)};
+#undef HCRC_DOWN_ROW
 const cal_up_fn kCalUp[TMAX] = {cal_up1_loads,          cal_up_mfma_loads<2>,  cal_up_mfma_loads<3>,
                                 cal_up_mfma_loads<4>,   cal_up_mfma_loads<5>,  cal_up_mfma_loads<6>,
                                 cal_up_mfma_loads<7>,   cal_up_mfma_loads<8>,  cal_up_mfma_loads<9>,
@@ -222,10 +336,10 @@ const up_fn kUpMfma[TMAX] = {
 }  // namespace hcr
 
 extern "C" int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
-                               const void* scratch, const float* x, void* stream) {
+                               void* scratch, const float* x, void* stream) {
   using namespace hcr;
-  if ((kind != HCRC_EMPTY && kind != HCRC_LOADS) || T < 1 || T > TMAX) return HCR_EINVAL;
-  if (kind == HCRC_LOADS) {
+  if ((kind != HCRC_EMPTY && kind != HCRC_LOADS && kind != HCRC_LOADS_STORE) || T < 1 || T > TMAX) return HCR_EINVAL;
+  if (kind != HCRC_EMPTY) {
     if (!w_down || !w_up || !w_norm || !scratch || !x) return HCR_EINVAL;
     if (!aligned(w_down, 16) || !aligned(w_up, 16) || !aligned(w_norm, 16) || !aligned(scratch, 256) ||
         !aligned(x, 16))
@@ -239,8 +353,10 @@ extern "C" int hcrc_read_floor(int kind, int T, const void* w_down, const void* 
     hipLaunchKernelGGL(cal_empty, dim3(UP_WGS), dim3(up_threads), 0, st);
   } else {
     const float* part = reinterpret_cast<const float*>(static_cast<const char*>(scratch) + OFF_PART);
-    hipLaunchKernelGGL(kCalDown[T - 1], dim3(DOWN_WGS), dim3(down_threads(T)), 0, st,
-                       static_cast<const uint16_t*>(w_down), x, w_norm);
+    float* lo = reinterpret_cast<float*>(static_cast<char*>(scratch) + OFF_LO);
+    static_assert(DOWN_WGS <= TMAX * R, "one store per down work-group fits the lo slot");
+    hipLaunchKernelGGL(kCalDown[kind == HCRC_LOADS_STORE][T - 1], dim3(DOWN_WGS), dim3(down_threads(T)), 0, st,
+                       static_cast<const uint16_t*>(w_down), x, w_norm, lo);
     hipLaunchKernelGGL(kCalUp[T - 1], dim3(UP_WGS), dim3(up_threads), 0, st, static_cast<const uint16_t*>(w_up),
                        part);
   }
@@ -263,5 +379,24 @@ extern "C" int hcrc_up_kernel(int kind, int T, const void* w_up, void* scratch, 
   else
     hipLaunchKernelGGL(kUpMfma[T - 1], dim3(UP_WGS), dim3(upm_threads(T)), 0, reinterpret_cast<hipStream_t>(stream),
                        w_up, nullptr, part, nullptr, nullptr, out, mean, lo);
+  return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}
+
+extern "C" int hcrc_slab_pair(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
+                              void* slab_scratch, const float* x, void* stream) {
+  using namespace hcr;
+  if ((kind != HCRC_SLAB_LOADS && kind != HCRC_SLAB_STORES && kind != HCRC_SLAB_FINISH) || T < 1 || T > 8)
+    return HCR_EINVAL;
+  if (!w_down || !w_up || !w_norm || !slab_scratch || !x) return HCR_EINVAL;
+  if (!aligned(w_down, 16) || !aligned(w_up, 16) || !aligned(w_norm, 16) || !aligned(slab_scratch, 256) ||
+      !aligned(x, 16))
+    return HCR_EALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* sc = static_cast<char*>(slab_scratch);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kSlabDown[kind][T - 1], dim3(SLABS * SLAB_GROUPS), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w_down), x, w_norm, sc);
+  hipLaunchKernelGGL(kSlabUp[T - 1], dim3(UP_WGS), dim3(upm_threads(T < 2 ? 2 : T)), 0, st,
+                     static_cast<const uint16_t*>(w_up), static_cast<const char*>(sc));
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }

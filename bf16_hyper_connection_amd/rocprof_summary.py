@@ -65,6 +65,12 @@ def kernel_key(name):
     m = re.search(r"cal_up_(valu|mfma)<(\d+)>", name)
     if m:
         return ("cal_up_" + m.group(1), int(m.group(2)))
+    m = re.search(r"cal_slab_down<(\d+), (\d+)>", name)
+    if m:
+        return ("cal_slab_down", int(m.group(1)), int(m.group(2)))
+    m = re.search(r"cal_slab_up<(\d+)>", name)
+    if m:
+        return ("cal_slab_up", int(m.group(1)))
     return None
 
 
@@ -315,6 +321,16 @@ def main():
                                                              "mfma_us": round(dur[km][0], 3)}
             ab_lines.append(f"| {T} | {dur[kv][0]:.3f} | {dur[km][0]:.3f} | {dur[km][0] - dur[kv][0]:+.3f} | "
                             f"{'matrix cores' if T >= 2 else 'vector ALUs'} |")
+    slab_lines = []
+    for T in range(1, 9):
+        ks = [("cal_slab_down", T, k) for k in range(3)]
+        if all(k in dur for k in ks) and ("cal_slab_up", T) in dur:
+            rec.setdefault("slab_probe", {})[str(T)] = {"down_loads_us": round(dur[ks[0]][0], 3),
+                                                        "down_stores_us": round(dur[ks[1]][0], 3),
+                                                        "down_finish_us": round(dur[ks[2]][0], 3),
+                                                        "up_lo_loads_us": round(dur[("cal_slab_up", T)][0], 3)}
+            slab_lines.append(f"| {T} | {dur[ks[0]][0]:.3f} | {dur[ks[1]][0]:.3f} | {dur[ks[2]][0]:.3f} | "
+                              f"{dur[ks[2]][0] - dur[ks[1]][0]:+.3f} | {dur[('cal_slab_up', T)][0]:.3f} |")
     if ("cal_empty",) in dur:
         rec["cal_empty_avg_us"] = round(dur[("cal_empty",)][0], 3)
     if cal_lines:
@@ -329,6 +345,13 @@ def main():
                    "`cal_up_mfma<T>` = hc_up_mfma's body; BF16, no pending write or injection), average µs per "
                    "dispatch:", "", "| T | vector ALUs (v_dot2) | matrix cores | difference | the read dispatches |",
                "|---|---|---|---|---|"] + ab_lines
+    if slab_lines:
+        md += ["", "The pages' down shape as probes (`hcrc_slab_pair`: 10 rows x a 1,280-column slab, 256 work-groups; "
+                   "the up grid loading lo only), average µs per dispatch of the down kernel: its loads, + its "
+                   "partial stores, + the last-arriver finish (agent-scope acquire-release counter, the 8th "
+                   "work-group of a row group sums the 8 slabs):", "",
+               "| T | loads | + stores | + finish | the finish's cost | up kernel loading lo |", "|---|---|---|---|---|---|"]
+        md += slab_lines
     if q in dur:
         md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
                    f"{dur[q][1]} calls."]

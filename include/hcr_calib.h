@@ -19,15 +19,20 @@
  *               every loaded value and discard it: no arithmetic, no LDS, no
  *               barrier, no store.
  *
+ *   HCRC_LOADS_STORE  HCRC_LOADS with one 4-byte store per down work-group,
+ *               issued before its loads (into scratch's lo slot): the fixed
+ *               cost of a kernel that writes memory at all.
+ *
  * The difference between the read and HCRC_LOADS is what the read's arithmetic,
  * reductions, LDS staging, barriers and stores add to its bare memory traffic.
  *
  * hcrc_read_floor: enqueue the pair `kind` for T tokens (1..HCR_T_MAX) on
  * `stream` (a hipStream_t; NULL is the null stream).  The pointers are those of
  * a read (include/hcr.h layouts): w_down and w_up BF16, w_norm float [4][2560],
- * scratch of hcr_scratch_bytes() bytes (its partials are loaded, never written),
- * x float [T][4][2560]; all device pointers, 16-byte aligned (scratch 256),
- * only read.  HCRC_EMPTY ignores them (they may be NULL).  No allocation, no
+ * scratch of hcr_scratch_bytes() bytes (its partials are loaded; only
+ * HCRC_LOADS_STORE writes, 256 floats into its lo slot), x float [T][4][2560];
+ * all device pointers, 16-byte aligned (scratch 256), otherwise only read.
+ * HCRC_EMPTY ignores them (they may be NULL).  No allocation, no
  * memset; graph-capturable.
  * Errors: HCR_EINVAL (unknown kind, T out of range, a NULL pointer for
  * HCRC_LOADS), HCR_EALIGN (both before any HIP call), HCR_EHIP.
@@ -39,10 +44,10 @@
 extern "C" {
 #endif
 
-enum { HCRC_EMPTY = 0, HCRC_LOADS = 1 };
+enum { HCRC_EMPTY = 0, HCRC_LOADS = 1, HCRC_LOADS_STORE = 2 };
 
-int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm,
-                    const void* scratch, const float* x, void* stream);
+int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const float* w_norm, void* scratch,
+                    const float* x, void* stream);
 
 /*
  * hcrc_up_kernel: enqueue one of the read's two up-projection kernels alone, for
@@ -64,6 +69,36 @@ int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const
 enum { HCRC_UP_VALU = 0, HCRC_UP_MFMA = 1 };
 
 int hcrc_up_kernel(int kind, int T, const void* w_up, void* scratch, float* out, float* mean, void* stream);
+
+/*
+ * hcrc_slab_pair: the load pattern of Strata PR #2812's down kernel (What
+ * changed: a work-group of rows over a 1,280-column slab, half a stream, and
+ * the last work-group of a row group to arrive finishing the split reduction;
+ * Extra Notes: the (2, 80) shape) on MI355X, to price its finish against the
+ * read's design.  Down: 256 work-groups of 10 rows x one 1,280-column slab
+ * (the 8 slabs of a row group on one XCD, work-group b % 8 = row group % 8),
+ * 4 waves, every lane 4 + 1 columns, loading x (T tokens), w_norm and its 10
+ * weight rows; up: the read's up grid loading lo only (not 4 stream partials)
+ * and its W_up tile.  No arithmetic; loaded values are discarded.
+ *   HCRC_SLAB_LOADS   the loads only;
+ *   HCRC_SLAB_STORES  + every down work-group stores its 10 T partials and T
+ *                     sums of squares;
+ *   HCRC_SLAB_FINISH  + the finish: after its stores a work-group increments
+ *                     its row group's counter (one agent-scope acquire-release
+ *                     atomic, no spinning); the 8th to arrive reads the 8
+ *                     slabs' partials and sums of squares, writes lo and
+ *                     resets the counter.
+ * slab_scratch: HCRC_SLAB_SCRATCH_BYTES bytes, 256-byte aligned, zero-filled
+ * before the first call (the counters; the finish leaves them at zero), used
+ * by one stream at a time.  w_down, w_up (BF16), w_norm, x: as for
+ * hcrc_read_floor.  T in 1..8.  Errors: HCR_EINVAL, HCR_EALIGN (before any HIP
+ * call), HCR_EHIP.
+ */
+enum { HCRC_SLAB_LOADS = 0, HCRC_SLAB_STORES = 1, HCRC_SLAB_FINISH = 2 };
+#define HCRC_SLAB_SCRATCH_BYTES (256u * 1024u)
+
+int hcrc_slab_pair(int kind, int T, const void* w_down, const void* w_up, const float* w_norm, void* slab_scratch,
+                   const float* x, void* stream);
 
 #ifdef __cplusplus
 }

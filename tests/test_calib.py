@@ -25,13 +25,15 @@ def cal():
     L.hcrc_read_floor.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
     L.hcrc_up_kernel.restype = ctypes.c_int
     L.hcrc_up_kernel.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+    L.hcrc_slab_pair.restype = ctypes.c_int
+    L.hcrc_slab_pair.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp]
     return L
 
 
 def test_exports_every_declared_symbol(cal):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(hcrc_[a-z_]+)\s*\(", text)))
-    assert names == ["hcrc_read_floor", "hcrc_up_kernel"]
+    assert names == ["hcrc_read_floor", "hcrc_slab_pair", "hcrc_up_kernel"]
     for n in names:
         assert hasattr(cal, n)
 
@@ -40,7 +42,7 @@ FAKE = dict(wd=0x10000000, wu=0x20000000, wn=0x30000000, sc=0x40000000, x=0x5000
 
 
 @pytest.mark.parametrize("kind,T,kw,rc", [
-    (2, 1, {}, HCR_EINVAL),            # unknown kind
+    (3, 1, {}, HCR_EINVAL),            # unknown kind
     (-1, 1, {}, HCR_EINVAL),
     (0, 0, {}, HCR_EINVAL),            # T out of range
     (1, 17, {}, HCR_EINVAL),
@@ -79,6 +81,15 @@ def test_pairs_run_and_write_nothing(cal, T):
     torch.cuda.synchronize()
     for a, b in zip(snap, (r.w_down, r.w_up, r.w_norm, r.scratch, x)):
         assert torch.equal(a, b)
+    # HCRC_LOADS_STORE writes one float per down work-group into the lo slot, nothing else
+    rc = cal.hcrc_read_floor(2, T, r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(), r.scratch.data_ptr(),
+                             x.data_ptr(), st)
+    assert rc == HCR_OK
+    torch.cuda.synchronize()
+    lo_off = hcr.hcr_scratch_layout()[0]
+    f = r.scratch.view(torch.float32)
+    assert torch.all(f[lo_off // 4: lo_off // 4 + 256] == 1.0)
+    assert torch.equal(r.scratch[:lo_off], snap[3][:lo_off]) and torch.equal(r.scratch[lo_off + 1024:], snap[3][lo_off + 1024:])
     assert np.isfinite(x.cpu().numpy()).all()
 
 
@@ -129,3 +140,49 @@ def test_up_kernels_alone_reproduce_the_read(cal, T):
     other = got[1 - dispatched]
     assert float((other[0] - ref_o).abs().max()) <= 1e-5 * scale
     assert float((other[1] - ref_m).abs().max()) <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("kind,T,kw,rc", [
+    (3, 1, {}, HCR_EINVAL),
+    (0, 0, {}, HCR_EINVAL),
+    (2, 9, {}, HCR_EINVAL),
+    (1, 2, dict(x=None), HCR_EINVAL),
+    (2, 2, dict(sc=0x40000010), HCR_EALIGN),
+    (0, 2, dict(wd=0x10000008), HCR_EALIGN),
+])
+def test_slab_pair_rejects_before_any_hip_call(cal, kind, T, kw, rc):
+    a = dict(FAKE)
+    a.update(kw)
+    assert cal.hcrc_slab_pair(kind, T, a["wd"], a["wu"], a["wn"], a["sc"], a["x"], None) == rc
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_slab_finish_protocol(cal, T):
+    """The last-arriver finish of the slab probe: after each call every counter is back to zero, and lo holds
+    what the 8th work-group of each row group computed from the 8 slabs' partials (thread t * 10 + r stored
+    10 t + r; sums of squares 1): lo[t][r] = 8 (10 t + r mod 10)."""
+    import torch
+
+    from bf16_hyper_connection_amd import inputs as gen
+    from tests.gpu_util import dev, reader_for, to_dev
+
+    print(f"slab pair T={T}", flush=True)
+    r = reader_for(gen.weight_set(0, 2))
+    x = to_dev(gen.activations(2, T))
+    sc = torch.zeros(256 * 1024, dtype=torch.uint8, device=dev())
+    st = torch.cuda.current_stream().cuda_stream
+    for rep in range(3):
+        for kind in (0, 1, 2):
+            rc = cal.hcrc_slab_pair(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(),
+                                    sc.data_ptr(), x.data_ptr(), st)
+            assert rc == HCR_OK
+    torch.cuda.synchronize()
+    f = sc.view(torch.float32)
+    ss_off, ctr_off = 8 * 16 * 320 * 4, 8 * 16 * 320 * 4 + 8 * 16 * 4 + 256
+    lo_off = ctr_off + 256
+    assert torch.all(sc.view(torch.int32)[ctr_off // 4: ctr_off // 4 + 32] == 0)
+    lo = f[lo_off // 4: lo_off // 4 + T * 320].view(T, 320).cpu()
+    t = torch.arange(T).view(T, 1).float()
+    rr = (torch.arange(320) % 10).view(1, 320).float()
+    assert torch.equal(lo, 8.0 * (10.0 * t + rr))
