@@ -617,6 +617,21 @@ def main():
                                         "the bound of prefetching the next read's weights into the MALL")
         log(f"bench: window with MALL-resident weights {window['mall_resident_us_per_window']} us")
         del gh
+        # the same 96 reads (weights, pending write, T = 6) without the chain: every read takes x0, so the
+        # chain's cost over independent reads is the difference
+        gi = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gi, stream=stream):
+                for i, r in enumerate(wreaders):
+                    r.read(wx0, wpend[i], None, out=wouts[i], mean=wmeans[i])
+        torch.cuda.current_stream().wait_stream(stream)
+        ims = timed(gi, reps, 3) / reps
+        window["unchained_us_per_window"] = round(ims * 1000, 2)
+        window["unchained_note"] = ("the same 96 reads (weights, pending write, T = 6) with x0 as every read's x: "
+                                    "no residual chain")
+        log(f"bench: the same reads unchained {window['unchained_us_per_window']} us")
+        del gi
 
     line = {
         "metric": METRIC, "value": round(us_per_read, 3), "unit": "µs", "n_gpus": 1,

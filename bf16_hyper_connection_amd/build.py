@@ -60,10 +60,12 @@ def _code_only(text):
 
 
 def source_hash():
-    """sha256 over the code of the library's sources (csrc/ and include/hcr.h), comments and whitespace
-    left out; measurements taken with hardware counters are valid only for the code they were taken on."""
+    """sha256 over the code of libhcr.so's sources (its csrc/ files and headers, and include/hcr.h; not the
+    calibration library's), comments and whitespace left out; measurements taken with hardware counters
+    are valid only for the code they were taken on."""
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    files = sorted(f for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".h", ".cpp")) and f not in CALIB_SOURCES)
     paths = [os.path.join(CSRC, f) for f in files] + [os.path.join(ROOT, "include", "hcr.h")]
     for path in paths:
         with open(path) as fh:
