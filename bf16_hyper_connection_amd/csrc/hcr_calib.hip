@@ -5,8 +5,9 @@
 // The load kernels repeat the index arithmetic of hc_down<T, FMT_BF16> and of the up kernel the read
 // dispatches at T (hc_up at T = 1, hc_up_mfma from T = 2) in hcr_kernels.hip: the same work-group
 // maps (down_stream / down_group, up_tile), lane ownership, load widths, load order and cache policy
-// (non-temporal weight loads).  Every loaded register is handed to an empty asm statement, so the
-// compiler keeps the load and waits for it, and nothing else is done with it.
+// (non-temporal weight loads; hc_up_mfma's weights straight into LDS with 3 waves).  Every loaded register
+// is handed to an empty asm statement, so the compiler keeps the load and waits for it, and nothing else is
+// done with it.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -111,7 +112,9 @@ __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t
   }
 }
 
-// hc_up_mfma<T>'s loads (T >= 2): partials, then one 16-row tile of W_up per wave, 10 K steps
+// hc_up_mfma<T>'s loads (T >= 2): partials, then one 16-row tile of W_up per wave.  With 3 waves (T < 10)
+// the weights go straight into LDS through load_a_lds, the read's own function (10 loads per wave); with a
+// 4th wave into registers in the operand layout (10 K steps).
 template <int T>
 __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
                                                          const float* __restrict__ part) {
@@ -119,9 +122,7 @@ __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restr
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;
   const int li = lane & 15, lg = lane >> 4;
-  const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
-  const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
-  constexpr bool NTW = NT == 192;
+  constexpr bool ALDS = NT == 192;
   // the partials first (issued before the weights, consumed after them, as in the read)
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + NT - 1) / NT;
@@ -131,20 +132,35 @@ __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restr
     const int it = min(tid + n * NT, ITEMS - 1);
     const int t = it / (R / 4), k = 4 * (it % (R / 4));
 #pragma unroll
-    for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
+    for (int ss = 0; ss < S; ++ss)
+      pv[n][ss] = ALDS ? ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k) : ld4(part + ((size_t)ss * TMAX + t) * R + k);
   }
   __builtin_amdgcn_sched_barrier(0);
-  uint4 a[R / 32];
+  constexpr int A_REGION = 10 * A_LOAD_STRIDE;
+  __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];
+  uint4 a[ALDS ? 1 : R / 32];
+  if constexpr (ALDS) {
+    load_a_lds<A_REGION>(w_up, lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave), lane, c0);
+    vm_wait<0>();
 #pragma unroll
-  for (int m = 0; m < R / 32; ++m)
-    a[m] = NTW ? ldw16(w_up + j * R + 32 * m + 8 * lg) : *reinterpret_cast<const uint4*>(w_up + j * R + 32 * m + 8 * lg);
+    for (int n = 0; n < NI; ++n)
+#pragma unroll
+      for (int ss = 0; ss < S; ++ss) vm_pin(pv[n][ss]);
+  } else {
+    const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
+    const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+#pragma unroll
+    for (int m = 0; m < R / 32; ++m) a[m] = *reinterpret_cast<const uint4*>(w_up + j * R + 32 * m + 8 * lg);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int n = 0; n < NI; ++n)
 #pragma unroll
     for (int ss = 0; ss < S; ++ss) use(pv[n][ss]);
+  if constexpr (!ALDS) {
 #pragma unroll
-  for (int m = 0; m < R / 32; ++m) use(a[m]);
+    for (int m = 0; m < R / 32; ++m) use(a[m]);
+  }
 }
 
 // hc_up<1>'s loads: partials, then 5 iterations of two rows per wave (16 + 4 bytes per lane and row)

@@ -58,6 +58,52 @@ __device__ __forceinline__ uint32_t ldw4(const void* p) { return __builtin_nonte
 __device__ __forceinline__ uint32_t ldw2(const void* p) { return __builtin_nontemporal_load(static_cast<const uint16_t*>(p)); }
 __device__ __forceinline__ uint32_t ldw1(const void* p) { return __builtin_nontemporal_load(static_cast<const uint8_t*>(p)); }
 
+// Loads whose completion the compiler does not track, for a kernel that waits for them itself (vm_wait).
+// The compiler's wait insertion gives up on in-order completion as soon as a load straight into LDS is in
+// flight: the first use of any older load then waits for every load, LDS ones included.  A kernel that
+// streams its weights into LDS while it works on earlier loads issues all of its vector-memory loads
+// through these instead, in a fixed order and number, and places each wait itself (vmcnt counts loads in
+// issue order: vmcnt(n) leaves only the n youngest in flight).  The results are plain asm outputs: a caller
+// pins them (vm_pin) after the wait that covers them, so that no use moves above it.
+__device__ __forceinline__ f32x4 ld4_untracked(const float* p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ float ld1_untracked(const float* p) {
+  float v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// A non-temporal 16-byte load straight into LDS (global_load_lds_dwordx4, no registers): lane l's 16 bytes
+// land at LDS byte address lds + 16 l; lds is one value for the whole wave, passed in M0 (an input of the asm,
+// so the compiler sets M0 and knows it; the load needs one wait state after that write).
+__device__ __forceinline__ void ldw16_lds_untracked(const void* p, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(p), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// vm_wait<n> for an n that is a constant only after unrolling (0 <= n <= 15)
+__device__ __forceinline__ void vm_wait_n(int n) {
+  switch (n) {
+    case 0: vm_wait<0>(); break;   case 1: vm_wait<1>(); break;   case 2: vm_wait<2>(); break;
+    case 3: vm_wait<3>(); break;   case 4: vm_wait<4>(); break;   case 5: vm_wait<5>(); break;
+    case 6: vm_wait<6>(); break;   case 7: vm_wait<7>(); break;   case 8: vm_wait<8>(); break;
+    case 9: vm_wait<9>(); break;   case 10: vm_wait<10>(); break; case 11: vm_wait<11>(); break;
+    case 12: vm_wait<12>(); break; case 13: vm_wait<13>(); break; case 14: vm_wait<14>(); break;
+    default: vm_wait<0>(); break;  // n > 14: the strictest wait
+  }
+}
+template <typename V>
+__device__ __forceinline__ void vm_pin(V& v) { asm volatile("" : "+v"(v)); }
+// the LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 
 __device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }

@@ -238,6 +238,25 @@ __device__ __forceinline__ bf16x8 codes_bf16(uint2 q) {
 }
 constexpr int SC_WORDS = S * UP_COLS * (R / Q8_BLOCK) / 2;  // 200 dwords of binary16 scales per work-group
 
+// The BF16 weight loads of hc_up_mfma (described there) for tile `wave` of the work-group at column c0:
+// 10 loads straight into the wave's LDS region at a_sm, untracked (the kernel waits for them itself).
+// Load i of a wave lands at byte i * A_LOAD_STRIDE of its region: 1024 bytes, then 128 of padding, so that
+// odd loads start 128 bytes into a 256-byte LDS row and even loads at its start.
+constexpr int A_LOAD_STRIDE = 1024 + 128;
+template <int A_REGION>
+__device__ __forceinline__ void load_a_lds(const uint16_t* __restrict__ w_up, uint32_t a_sm, int wave, int lane,
+                                           int c0) {
+  const int rho = lane >> 3, e = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int p = i >> 1, h = i & 1;
+    int rw = 16 * wave + 8 * h + rho;
+    rw = rw < UP_ROWS ? rw : rw - 8;
+    const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
+    ldw16_lds_untracked(w_up + j * R + 8 * (8 * p + (e ^ rho)), a_sm + wave * A_REGION + i * A_LOAD_STRIDE);
+  }
+}
+
 // up on the matrix cores (BF16 weights from T = UP_MFMA_FROM, Q8_0 copies from T = UP_MFMA_FROM_Q8).  The
 // same work-group tile as hc_up (10 columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves
 // 0..2; rows 40..47 repeat row 39 and are not stored) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K
@@ -262,10 +281,25 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const int li = lane & 15, lg = lane >> 4;
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
   //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes
+  //    BF16 with 3 waves (T < 10, ALDS): every load of the kernel is untracked (ld*_untracked: the weights
+  //    go straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.
+  constexpr bool NTW = UPM_THREADS == 192;
+  constexpr bool ALDS = !Q8 && NTW;
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
-  load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
+  if constexpr (ALDS) {
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {  // load_partials' items and order
+      const int it = min(tid + n * UPM_THREADS, ITEMS - 1);
+      const int t = it / (R / 4), k = 4 * (it % (R / 4));
+#pragma unroll
+      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
+      if (INJ) iv[n] = ld4_untracked(inj + (size_t)t * R + k);
+    }
+  } else {
+    load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
+  }
   constexpr int NSC = Q8 ? (SC_WORDS + UPM_THREADS - 1) / UPM_THREADS : 0;
   uint32_t scw[NSC > 0 ? NSC : 1];
 #pragma unroll
@@ -279,31 +313,57 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const bool eok = wave < 3 && cc < UP_COLS && li < T;
   float pend[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-    pend[s] = PEND ? pending[((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1)] : 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* pp = pending + ((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1);
+    pend[s] = !PEND ? 0.f : ALDS ? ld1_untracked(pp) : *pp;
+  }
   __builtin_amdgcn_sched_barrier(0);  // keeps every small load ahead of the weight loads
-  // 2. weights (A operand): tile = wave, row rw = 16 * wave + li, K 32 m + 8 lg.  No load is conditional:
-  //    rows 40..47 of the third tile re-load row 39, and a 4th wave (T >= 10) re-loads the third tile's
-  //    rows, cache hits whose results are never stored.  A branch around loads, even a wave-uniform one,
-  //    makes the compiler wait for them before the first barrier, serialising the weight stream with the
-  //    lo staging.
-  const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
-  // non-temporal weight loads (ldw*), except with a 4th wave: its repeats of the third tile's rows are separate
-  // load instructions, which then missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16)
-  constexpr bool NTW = UPM_THREADS == 192;
-  const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
-  uint4 a[Q8 ? 1 : R / 32];   // BF16: 8 weights per step
-  uint2 qa[Q8 ? R / 32 : 1];  // Q8_0: 8 codes per step
+  // 2. weights (A operand), tile = wave: row rw = 16 * wave + li of the work-group's 40 (rw & 3 = stream,
+  //    rw >> 2 = column), K chunk (8 values) 4 m + lg at step m.
+  //    ALDS: straight into LDS (global_load_lds_dwordx4, non-temporal), each wave into a region of its own
+  //    that only it reads back, so no barrier guards it.  Load i = 2 p + h of a wave covers tile rows
+  //    8 h .. 8 h + 7 and line p (K 64 p .. 64 p + 63) of each: lane 8 rho + e takes chunk 8 p + (e ^ rho) of
+  //    row 8 h + rho, so every 16 lanes read two whole 128-byte lines (in the operand layout every 16 lanes
+  //    touch 16 rows, 16 bytes each: twice the requests, measured 0.3-0.4 us slower per read).  Load i lands
+  //    at byte i * 1152 of the region (A_LOAD_STRIDE), so the 8 rows of load 2 p sit at 0 and those of load
+  //    2 p + 1 at 128 modulo 256: the read-back of one chunk's 16 rows meets 16 distinct LDS bank groups.  The
+  //    third tile's rows 40..47 load rows 32..39 again (their products are not stored).
+  //    Otherwise in the operand layout, into registers: lane (li, lg) loads row rw, K 32 m + 8 lg.  No load
+  //    is conditional: rows 40..47 of the third tile re-load row 39, and a 4th wave (T >= 10) re-loads the
+  //    third tile's rows, cache hits whose results are never stored (a branch around loads, even a
+  //    wave-uniform one, makes the compiler wait for them before the first barrier).  Non-temporal, except
+  //    with a 4th wave: its repeats of the third tile's rows are separate load instructions, which then
+  //    missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16).
+  constexpr int A_REGION = 10 * A_LOAD_STRIDE;
+  static_assert(R == 320, "5 lines of 128 bytes per BF16 row, 10 loads per wave");
+  __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];
+  uint4 a[ALDS || Q8 ? 1 : R / 32];  // BF16 in registers: 8 weights per step
+  uint2 qa[Q8 ? R / 32 : 1];         // Q8_0: 8 codes per step
+  if constexpr (ALDS) {
+    load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
+                         lane, c0);
+  } else {
+    const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
+    const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
 #pragma unroll
-  for (int m = 0; m < R / 32; ++m) {
-    if constexpr (Q8)
-      qa[m] = NTW ? ldw8(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg)
-                  : *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
-    else
-      a[m] = NTW ? ldw16(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg)
-                 : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
+    for (int m = 0; m < R / 32; ++m) {
+      if constexpr (Q8)
+        qa[m] = NTW ? ldw8(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg)
+                    : *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
+      else
+        a[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (ALDS) {  // the partials (and injection): all but the pending loads and the 10 weight loads
+    vm_wait<(PEND ? S : 0) + 10>();
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+#pragma unroll
+      for (int ss = 0; ss < S; ++ss) vm_pin(pv[n][ss]);
+      if (INJ) vm_pin(iv[n]);
+    }
+  }
 
   // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order.
   //    T <= 8 (PACK): one B matrix, column t < 8 = high parts of token t, column 8 + t = its low parts:
@@ -354,7 +414,19 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
-    const bf16x8 am = Q8 ? codes_bf16(qa[m]) : __builtin_bit_cast(bf16x8, a[Q8 ? 0 : m]);
+    bf16x8 am;
+    if constexpr (Q8) {
+      am = codes_bf16(qa[m]);
+    } else if constexpr (ALDS) {
+      // chunk 4 m + lg of tile row li: line p = m / 2, load 2 p + li / 8, lane 8 (li % 8) + (chunk % 8) ^ (li % 8);
+      // line p's two loads are done once no more than the 8 - 2 p weight loads after them are in flight
+      if (m % 2 == 0) vm_wait_n(8 - m);
+      const int h = li >> 3, r8 = li & 7, ep = (4 * m + lg) & 7;
+      am = *reinterpret_cast<const bf16x8*>(a_sm + wave * A_REGION + (2 * (m >> 1) + h) * A_LOAD_STRIDE +
+                                            16 * (8 * r8 + (ep ^ r8)));
+    } else {
+      am = __builtin_bit_cast(bf16x8, a[m]);
+    }
     f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bh[m][lg][li]), Q8 ? zero : acc, 0, 0, 0);
     if constexpr (!PACK)
       pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bl[m][lg][li]), pm, 0, 0, 0);
@@ -369,6 +441,10 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   if constexpr (PACK) {
 #pragma unroll
     for (int s = 0; s < S; ++s) acc[s] += dpp<0x128>(acc[s]);  // row_ror:8
+  }
+  if constexpr (ALDS && PEND) {  // the pending loads, older than the weight loads, are done since step 0's wait
+#pragma unroll
+    for (int s = 0; s < S; ++s) vm_pin(pend[s]);
   }
   // 5. epilogue: lane = token li, rows 16 wave + 4 lg + s = stream s of column 4 wave + lg; the stream
   //    mean in the v_dot2 kernel's order ((s0 + s1) + (s2 + s3))

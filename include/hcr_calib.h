@@ -15,9 +15,10 @@
  *               exactly the read's global loads at T, in the same order and with
  *               the same cache policy (down: the stream's x for the T tokens,
  *               w_norm, then the work-group's 5 rows of W_down; up: the 4 stream
- *               partials of lo, then the work-group's 40 rows of W_up), wait for
- *               every loaded value and discard it: no arithmetic, no LDS, no
- *               barrier, no store.
+ *               partials of lo, then the work-group's 40 rows of W_up, for
+ *               T = 2..9 straight into LDS as the read loads them), wait for
+ *               every loaded value and discard it: no arithmetic, no other LDS
+ *               access, no barrier, no store.
  *
  *   HCRC_LOADS_STORE  HCRC_LOADS with one 4-byte store per down work-group,
  *               issued before its loads (into scratch's lo slot): the fixed
