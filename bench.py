@@ -395,7 +395,7 @@ def main():
         calibration["read_over_loads_us"] = {T: round(per_T_us[T] - calibration["loads_pair_us"][T], 3)
                                              for T in range(1, T_WIDE + 1)}
         # the two up kernels alone, per T (graphs of 32, each on a set's W_up and scratch): the read dispatches
-        # the vector-ALU one at T = 1 and the matrix-core one from T = 2
+        # the matrix-core one at every T
         cal.hcrc_up_kernel.restype = ctypes.c_int
         cal.hcrc_up_kernel.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
         for kind, key in ((0, "up_valu_us"), (1, "up_mfma_us")):
@@ -642,7 +642,7 @@ def main():
                                "(419 MB), T = 1..8, one read per set and T per step, HIP graph replay",
                    "reads_per_step": reads_per_step, "weight_sets": len(readers),
                    "arithmetic": "bf16 weights; fp32 accumulation (down: FMA on widened weights; up: "
-                                 "v_mfma_f32_16x16x32_bf16 from T = 2, v_dot2_f32_bf16 at T = 1, with lo "
+                                 "v_mfma_f32_16x16x32_bf16 with lo "
                                  "split into bf16 high + low)",
                    "per_T_us": {T: v for T, v in per_T_us.items() if T <= TMAX},
                    "per_T_algorithmic_GBps": {T: v for T, v in per_T_gbps.items() if T <= TMAX},
@@ -659,7 +659,7 @@ def main():
                                          "gave the same bytes"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "the read (hc_down + hc_up_mfma / hc_up dispatches), event-timed per read over the "
+                     "kernel": "the read (hc_down + hc_up_mfma dispatches), event-timed per read over the "
                                "timed region; "
                                "traffic = counter-measured HBM bytes per read (mean over T = 1..8)"},
     }

@@ -3,7 +3,7 @@
 // (HCRC_LOADS).  Measurement only.
 //
 // The load kernels repeat the index arithmetic of hc_down<T, FMT_BF16> and of the up kernel the read
-// dispatches at T (hc_up at T = 1, hc_up_mfma from T = 2) in hcr_kernels.hip: the same work-group
+// dispatches for BF16 weights (hc_up_mfma at every T) in hcr_kernels.hip: the same work-group
 // maps (down_stream / down_group, up_tile), lane ownership, load widths, load order and cache policy
 // (non-temporal weight loads; hc_up_mfma's weights straight into LDS with 3 waves).  Every loaded register
 // is handed to an empty asm statement, so the compiler keeps the load and waits for it, and nothing else is
@@ -163,35 +163,6 @@ __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restr
   }
 }
 
-// hc_up<1>'s loads: partials, then 5 iterations of two rows per wave (16 + 4 bytes per lane and row)
-__global__ __launch_bounds__(UP_THREADS) void cal_up1_loads(const uint16_t* __restrict__ w_up,
-                                                            const float* __restrict__ part) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int h = lane >> 5, q = lane & 31;
-  const int c0 = up_tile(blockIdx.x) * UP_COLS;
-  constexpr int ITEMS = R / 4;
-  const int it = min(tid, ITEMS - 1), k = 4 * it;
-  f32x4 pv[S];
-#pragma unroll
-  for (int ss = 0; ss < S; ++ss) pv[ss] = ld4(part + (size_t)ss * TMAX * R + k);
-  __builtin_amdgcn_sched_barrier(0);
-  uint4 wa[UP_ITERS];
-  uint32_t wb[UP_ITERS];
-#pragma unroll
-  for (int m = 0; m < UP_ITERS; ++m) {
-    const int rw = UP_WAVE_ROWS * wave + 2 * m + h;
-    const uint16_t* row = w_up + ((size_t)(rw & 3) * D + c0 + (rw >> 2)) * R;
-    wa[m] = ldw16(row + 8 * q);
-    wb[m] = ldw4(row + 256 + 2 * q);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ss = 0; ss < S; ++ss) use(pv[ss]);
-#pragma unroll
-  for (int m = 0; m < UP_ITERS; ++m) use(wa[m]), use(wb[m]);
-}
-
-
 // ---- the pages' down-kernel shape and finish, as loads (and stores, and the finish) only
 // slab scratch: partials [8 slabs][TMAX][R] at 0, sums of squares [8][TMAX] at SLAB_OFF_SS, counters [32 row
 // groups] at SLAB_OFF_CTR, lo [TMAX][R] at SLAB_OFF_LO
@@ -310,13 +281,13 @@ static_assert(TMAX == 16, "the tables below list T = 1..16");
    cal_down_loads<16, F>}
 const cal_down_fn kCalDown[2][TMAX] = {HCRC_DOWN_ROW(false), HCRC_DOWN_ROW(true)};
 #undef HCRC_DOWN_ROW
-const cal_up_fn kCalUp[TMAX] = {cal_up1_loads,          cal_up_mfma_loads<2>,  cal_up_mfma_loads<3>,
+const cal_up_fn kCalUp[TMAX] = {cal_up_mfma_loads<1>,   cal_up_mfma_loads<2>,  cal_up_mfma_loads<3>,
                                 cal_up_mfma_loads<4>,   cal_up_mfma_loads<5>,  cal_up_mfma_loads<6>,
                                 cal_up_mfma_loads<7>,   cal_up_mfma_loads<8>,  cal_up_mfma_loads<9>,
                                 cal_up_mfma_loads<10>,  cal_up_mfma_loads<11>, cal_up_mfma_loads<12>,
                                 cal_up_mfma_loads<13>,  cal_up_mfma_loads<14>, cal_up_mfma_loads<15>,
                                 cal_up_mfma_loads<16>};
-static_assert(UP_MFMA_FROM == 2, "the read dispatches hc_up at T = 1 and hc_up_mfma from T = 2");
+static_assert(UP_MFMA_FROM == 1, "the read dispatches hc_up_mfma at every T for BF16 weights");
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 

@@ -38,6 +38,21 @@ __device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
+// the same split of 4 values
+__device__ __forceinline__ void split_hi_lo4(const f32x4& v, uint2& hi, uint2& lo) {
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const f32x2 a = {v[2 * e], v[2 * e + 1]};
+    const bf16x2 bh = __builtin_convertvector(a, bf16x2);
+    const f32x2 r = a - __builtin_convertvector(bh, f32x2);  // exact
+    const bf16x2 bl = __builtin_convertvector(r, bf16x2);
+    h[e] = __builtin_bit_cast(uint32_t, bh);
+    l[e] = __builtin_bit_cast(uint32_t, bl);
+  }
+  hi = make_uint2(h[0], h[1]);
+  lo = make_uint2(l[0], l[1]);
+}
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 

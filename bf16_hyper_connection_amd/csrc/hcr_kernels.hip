@@ -18,7 +18,7 @@
 //     (halving with v_permlane32/16_swap, then DPP; each group of four values
 //     as soon as its row is done) and over the waves (LDS, fixed order); the
 //     work-group writes rs[t][s] * (row sums), one partial per stream.
-//   hc_up_mfma<T, INJ, PEND> (BF16 weights from T = 2, Q8_0 copies from T = 4):
+//   hc_up_mfma<T, INJ, PEND> (BF16 weights at every T, Q8_0 copies from T = 4):
 //     lo[t][k] = the 4 stream
 //     partials (+ injection), then 40 rows of W_up (10 columns x 4 streams) per
 //     work-group as three 16-row tiles on the matrix cores
@@ -27,8 +27,8 @@
 //     parts columns 8..15, one product per K step; from 9 tokens each part has
 //     its own product.  Epilogue in the lane: pending write, sigmoid gate of
 //     lo[t][s], stream mean.
-//   hc_up<T, INJ, PEND>: the same tile on the vector ALUs (BF16 at T = 1,
-//     Q8_0 at T = 1..3).  Each row is reduced by the 32 lanes of a half-wave;
+//   hc_up<T, INJ, PEND>: the same tile on the vector ALUs (Q8_0 at T = 1..3;
+//     for BF16 only the calibration library runs it, to time it against the other).  Each row is reduced by the 32 lanes of a half-wave;
 //     lane q owns K [8q, 8q+8) and [256+2q, +2) and multiplies with
 //     v_dot2_f32_bf16 against the high and low parts of lo.  Epilogue: pending
 //     write, sigmoid gate, stream mean of 4 adjacent outputs (DPP quad).
@@ -39,18 +39,17 @@
 // FMA on widened weights instead: its activations change every row group, and
 // the split would cost more VALU than the widening.
 //
-// Why the matrix cores for the up projection from T = 2: the v_dot2 kernel
-// issues ~100 VALU instructions per token per wave, which the loads cannot
-// hide with one wave per SIMD; the matrix-core kernel's 10 or 20 MFMAs per
-// wave cost the same at every T.  Measured on MI355X, whole read: T = 1
-// 6.45 us (v_dot2) against 6.82 (matrix cores); when the matrix-core kernel
-// was introduced, T = 2 7.60 against 7.56 and T = 8 10.42 against 9.28.
+// Why the matrix cores for the BF16 up projection: the v_dot2 kernel issues
+// ~100 VALU instructions per token per wave, which the loads cannot hide with
+// one wave per SIMD; the matrix-core kernel's 10 or 20 MFMAs per wave cost the
+// same at every T.  With its weights loaded straight into LDS in whole lines it
+// is faster at T = 1 too: 6.18 against 6.25 us per read (whole read, one
+// process, alternating builds, 3 rounds).
 //
 // T = 10..16: the down kernel takes the tokens in groups of 8 (the next
 // group's x loads overlap the current group's FMAs); up to 9 in one group.  A token's result is the
-// same bit for bit at every T of one range: T = 2..8 and T = 9..16 (the two
-// B layouts round differently); a token read alone (T = 1, v_dot2) rounds
-// differently again.
+// same bit for bit at every T of one range: T = 1..8 and T = 9..16 (the two
+// B layouts round differently).
 //
 // Why no atomics: the pages finish the split reduction in the last
 // work-group to arrive at a counter.  On MI355X an agent-scope arrival
@@ -87,7 +86,7 @@
 //
 // Determinism: every sum has a fixed order, so repeated calls and graph
 // replays are bitwise identical, and each token's result does not depend on T
-// within T = 2..8 or within T = 9..16 (BF16), or within T = 1..3, 4..8 or
+// within T = 1..8 or within T = 9..16 (BF16), or within T = 1..3, 4..8 or
 // 9..16 (Q8_0).
 
 #include <hip/hip_runtime.h>

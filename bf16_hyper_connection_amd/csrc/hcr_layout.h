@@ -55,7 +55,7 @@ constexpr int UP_THREADS = 256;
 constexpr int UP_ROWS = UP_COLS * S;                         // 40
 constexpr int UP_WAVE_ROWS = UP_ROWS / (UP_THREADS / 64);    // 10
 constexpr int UP_ITERS = UP_WAVE_ROWS / 2;                   // 5 (two rows per iteration, one per half-wave)
-constexpr int UP_MFMA_FROM = 2;  // BF16 up projection of T >= 2 on the matrix cores (measured faster there)
+constexpr int UP_MFMA_FROM = 1;  // BF16 up projection on the matrix cores at every T (measured faster at T = 1 too)
 constexpr int UP_MFMA_FROM_Q8 = 4;  // the same for Q8_0 copies (their codes are widened per K step)
 // matrix-core up kernel: one 16-row tile of the 40 rows per wave (3 waves); from T = 10 a 4th wave (no tile)
 // halves the rounds of the lo staging, measured faster there

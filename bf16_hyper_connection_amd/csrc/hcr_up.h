@@ -365,18 +365,40 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     }
   }
 
-  // 3. lo = the 4 stream partials (+ inj), then its BF16 high/low parts in B operand order.
+  // 3. lo = the 4 stream partials (+ inj), item by item (the 4 K values of one token that load_partials'
+  //    order gives each thread), and its BF16 high and low parts straight into B operand order, 8 bytes
+  //    each (no round trip of lo through LDS):
   //    T <= 8 (PACK): one B matrix, column t < 8 = high parts of token t, column 8 + t = its low parts:
-  //      bh[m][g][n] = parts of lo[n & 7][32 m + 8 g .. + 8]
-  //    T > 8: bh[m][g][t] and bl[m][g][t] = high and low parts of lo[t][32 m + 8 g .. + 8].
-  //    Only the T tokens' columns are staged: a column of B reaches only the same column of the
-  //    product, and the columns of tokens >= T are never stored.
+  //      bh[m][g][n ^ sw] = parts of lo[n & 7][32 m + 8 g .. + 8]
+  //    T > 8: bh[m][g][t ^ sw] and bl[m][g][t ^ sw] = high and low parts of lo[t][32 m + 8 g .. + 8];
+  //    sw = (4 m + g) % 16.  A wave's items are consecutive K of one token: swizzled, each 32 of them write
+  //    32 distinct 8-byte slots of a 256-byte LDS row (unswizzled, every 16 would meet the same banks), and
+  //    the operand read of one (m, g) still takes 16 distinct 16-byte slots.  Only the T tokens' columns
+  //    are staged: a column of B reaches only the same column of the product, and the columns of tokens
+  //    >= T are never stored.  Items past the end (repeats of the last) write a junk slot of their thread.
   constexpr bool PACK = T <= 8;
-  __shared__ __attribute__((aligned(16))) float lo_sm[T * R + LO_JUNK];
   __shared__ uint4 bh[R / 32][4][16], bl[PACK ? 1 : R / 32][4][16];
-  __shared__ float gate_sm[T][S];
+  __shared__ uint2 b_junk[2 * UPM_THREADS];
+  __shared__ f32x4 lo4_sm[T];
   __shared__ __attribute__((aligned(16))) float sc_sm[Q8 ? 2 * SC_WORDS + 2 * 64 : 4];
-  store_lo<T, INJ, NI, UPM_THREADS>(tid, pv, iv, lo_sm);
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int it0 = tid + n * UPM_THREADS, it = min(it0, ITEMS - 1);
+    const int t = it / (R / 4), k = 4 * (it % (R / 4));
+    f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
+    if (INJ) vv += iv[n];
+    uint2 hi, lo;
+    split_hi_lo4(vv, hi, lo);
+    const int m = k >> 5, g = (k >> 3) & 3, half = (k >> 2) & 1, sw = (4 * m + g) & 15;
+    const bool real = it0 < ITEMS;
+    uint2* dh = real ? reinterpret_cast<uint2*>(&bh[m][g][t ^ sw]) + half : &b_junk[2 * tid];
+    uint2* dl = real ? reinterpret_cast<uint2*>(PACK ? &bh[m][g][(8 + t) ^ sw] : &bl[m][g][t ^ sw]) + half
+                     : &b_junk[2 * tid + 1];
+    *dh = hi;
+    *dl = lo;
+    if (real && k == 0) lo4_sm[t] = vv;  // lo[t][0 .. S), whose sigmoids are the gates
+    if (real && blockIdx.x == 0) *reinterpret_cast<f32x4*>(lo_out + t * R + k) = vv;
+  }
 #pragma unroll
   for (int n = 0; n < NSC; ++n) {  // scale u of stream ss: row c0 + u / 10, block u % 10; repeats to a junk slot
     const int it0 = tid + n * UPM_THREADS, it = min(it0, SC_WORDS - 1), ss = it / (SC_WORDS / S);
@@ -388,24 +410,18 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     }
   }
   __syncthreads();
-  for (int i = tid; i < (R / 32) * 4 * T; i += UPM_THREADS) {
-    const int t = i % T, g = (i / T) & 3, m = i / (4 * T);
-    float v8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v8[e] = lo_sm[t * R + 32 * m + 8 * g + e];
-    uint4 hi, lo;
-    split_hi_lo(v8, hi, lo);
-    bh[m][g][t] = hi;
-    if constexpr (PACK)
-      bh[m][g][8 + t] = lo;
-    else
-      bl[m][g][t] = lo;
-  }
-  if (tid < T * S) gate_sm[tid / S][tid % S] = 1.0f / (1.0f + expf(-lo_sm[(tid / S) * R + (tid % S)]));
-  if (blockIdx.x == 0)
-    for (int i = tid; i < T * R; i += UPM_THREADS) lo_out[i] = lo_sm[i];
-  __syncthreads();
   if (wave >= 3) return;
+  // the gates of the lane's token, sigmoid of lo[li][0 .. S), computed here while the weights still arrive
+  // (in the staging above, the few lanes holding K 0 of a token would hold up their whole waves)
+  float gate[S];
+  {
+    const f32x4 l4 = lo4_sm[min(li, T - 1)];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      gate[s] = 1.0f / (1.0f + expf(-l4[s]));
+      vm_pin(gate[s]);  // computed here, ahead of the first wait for the weights, not sunk into the epilogue
+    }
+  }
   // 4. the tile on the matrix cores, K in order (T > 8: high part then low part of each step, into the
   //    same accumulator; T <= 8: one product per step, then token t's high-part sum (column t) plus its
   //    low-part sum (column 8 + t, brought over by a rotation of the 16-lane row by 8).  Q8_0: each step
@@ -427,9 +443,10 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     } else {
       am = __builtin_bit_cast(bf16x8, a[m]);
     }
-    f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bh[m][lg][li]), Q8 ? zero : acc, 0, 0, 0);
+    const int bc = li ^ ((4 * m + lg) & 15);  // column li of B, swizzled as staged
+    f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bh[m][lg][bc]), Q8 ? zero : acc, 0, 0, 0);
     if constexpr (!PACK)
-      pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bl[m][lg][li]), pm, 0, 0, 0);
+      pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bl[m][lg][bc]), pm, 0, 0, 0);
     if constexpr (Q8) {
       const f32x4 dm = *reinterpret_cast<const f32x4*>(sc_sm + (min(cc, UP_COLS - 1) * (R / Q8_BLOCK) + m) * S);
 #pragma unroll
@@ -452,7 +469,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     float o[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      o[s] = gate_sm[li][s] * acc[s];
+      o[s] = gate[s] * acc[s];
       if (PEND) o[s] += pend[s];
       out[((size_t)li * S + s) * D + c0 + cc] = o[s];
     }

@@ -57,8 +57,6 @@ def kernel_key(name):
     m = re.search(r"cal_down_loads<(\d+)>", name)
     if m:
         return ("cal_down_loads", int(m.group(1)))
-    if "cal_up1_loads" in name:
-        return ("cal_up_loads", 1)
     m = re.search(r"cal_up_mfma_loads<(\d+)>", name)
     if m:
         return ("cal_up_loads", int(m.group(1)))
@@ -169,8 +167,8 @@ def sq_table(d, commands):
     from bf16_hyper_connection_amd.build import source_hash
     md = ["# SQ counters of the read kernels (MI355X)", "", "Commands (run from the repository root, on one MI355X):",
           "", "```"] + commands + ["```", "", f"Library sources sha256 {source_hash()[:16]}…", "",
-          "Medians per dispatch (BF16 weights, no pending write or injection; down = `hc_down`, up = `hc_up` at "
-          "T = 1, `hc_up_mfma` from T = 2), then per wave: WAIT_ANY (waiting on anything, mostly memory), "
+          "Medians per dispatch (BF16 weights, no pending write or injection; down = `hc_down`, up = "
+          "`hc_up_mfma`), then per wave: WAIT_ANY (waiting on anything, mostly memory), "
           "ACTIVE_INST_VALU (the wave's VALU issue) and WAIT_INST_ANY (an instruction ready but not issued: "
           "dependencies, or the other wave of the SIMD issuing). Counts are the counters' own units.", "",
           "| kernel | T | waves | wave cycles | WAIT_ANY | WAIT_INST_ANY | ACTIVE_INST_ANY | ACTIVE_INST_VALU | "
@@ -295,7 +293,7 @@ def main():
         rec["timed_region"].update(bench_event_us_per_read_untraced=untraced, bench_event_us_per_read_traced=traced)
         tot = tr[2] + tr[3]
         md += ["", f"Timed region of the traced bench run (its timed steps, found between two marker kernels): "
-                   f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + up (hc_up_mfma, hc_up at T = 1) {tr[3]:.3f} µs = "
+                   f"{tr[0]} reads; average dispatch duration hc_down {tr[2]:.3f} µs + hc_up_mfma {tr[3]:.3f} µs = "
                    f"{tot:.3f} µs per read (p10 / p50 / p90 of down + up per read: "
                    f"{tr[4][10]:.3f} / {tr[4][50]:.3f} / {tr[4][90]:.3f} µs)."
                    + (f" An untraced `python bench.py` of the same session measured {untraced:.3f} µs per read "
@@ -320,7 +318,7 @@ def main():
             rec.setdefault("up_kernels_alone", {})[str(T)] = {"valu_us": round(dur[kv][0], 3),
                                                              "mfma_us": round(dur[km][0], 3)}
             ab_lines.append(f"| {T} | {dur[kv][0]:.3f} | {dur[km][0]:.3f} | {dur[km][0] - dur[kv][0]:+.3f} | "
-                            f"{'matrix cores' if T >= 2 else 'vector ALUs'} |")
+                            "matrix cores |")
     slab_lines = []
     for T in range(1, 9):
         ks = [("cal_slab_down", T, k) for k in range(3)]

@@ -18,13 +18,12 @@
  *   mean[t,c]  = (1/4) * sum_s out[t,s,c]
  *
  * T may be 0..16 (the pages' windows are 1..8 tokens; 9..16 serve larger windows).
- * Arithmetic is FP32 (BF16 weights are widened exactly; for T >= 2 the up
- * projection of BF16 weights runs on the matrix cores with lo split into BF16
- * high and low parts); summation orders are fixed, so a call is bitwise
- * reproducible, also as a replayed HIP graph.  A token's results are the same
- * bit for bit whatever the other tokens of the window within one range of T:
- * BF16 weights T = 2..8 and T = 9..16 (a token read alone, T = 1, rounds
- * differently), Q8_0 copies T = 1..3, 4..8 and 9..16.
+ * Arithmetic is FP32 (BF16 weights are widened exactly; the up projection of
+ * BF16 weights runs on the matrix cores with lo split into BF16 high and low
+ * parts); summation orders are fixed, so a call is bitwise reproducible, also
+ * as a replayed HIP graph.  A token's results are the same bit for bit
+ * whatever the other tokens of the window within one range of T: BF16 weights
+ * T = 1..8 and T = 9..16, Q8_0 copies T = 1..3, 4..8 and 9..16.
  *
  * Memory. Every pointer is a device pointer the caller owns (the library
  * allocates nothing on the device and never frees caller memory).  Layouts

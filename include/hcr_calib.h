@@ -51,11 +51,12 @@ int hcrc_read_floor(int kind, int T, const void* w_down, const void* w_up, const
                     const float* x, void* stream);
 
 /*
- * hcrc_up_kernel: enqueue one of the read's two up-projection kernels alone, for
- * T tokens (1..HCR_T_MAX), BF16 weights, no pending write or injection, so that
- * the two can be timed against each other at every T (the read dispatches the
- * vector-ALU kernel at T = 1 and the matrix-core kernel from T = 2; Strata PR
- * #2812's up kernel is the basis of both, What changed):
+ * hcrc_up_kernel: enqueue one of the library's two up-projection kernels alone,
+ * for T tokens (1..HCR_T_MAX), BF16 weights, no pending write or injection, so
+ * that the two can be timed against each other at every T (the read dispatches
+ * the matrix-core kernel at every T for BF16 weights, the vector-ALU one serves
+ * Q8_0 copies at T = 1..3; Strata PR #2812's up kernel is the basis of both,
+ * What changed):
  *   HCRC_UP_VALU  hc_up (v_dot2_f32_bf16 on lo split into BF16 high and low parts)
  *   HCRC_UP_MFMA  hc_up_mfma (v_mfma_f32_16x16x32_bf16, the same split)
  * w_up: BF16 [10240][320]; scratch: a handle's scratch (hcr_scratch_bytes()
