@@ -112,17 +112,17 @@ __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t
   }
 }
 
-// hc_up_mfma<T>'s loads (T >= 2): partials, then one 16-row tile of W_up per wave.  With 3 waves (T < 10)
-// the weights go straight into LDS through load_a_lds, the read's own function (10 loads per wave); with a
-// 4th wave into registers in the operand layout (10 K steps).
+// hc_up_mfma<T>'s loads: partials, then one 16-row tile of W_up per wave.  Below T = 10 the weights go
+// straight into LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads none);
+// from T = 10 into registers in the operand layout (10 K steps).
 template <int T>
 __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
                                                          const float* __restrict__ part) {
-  constexpr int NT = upm_threads(T);
+  constexpr int NT = upm_threads(T, FMT_BF16);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;
   const int li = lane & 15, lg = lane >> 4;
-  constexpr bool ALDS = NT == 192;
+  constexpr bool ALDS = T < 10;
   // the partials first (issued before the weights, consumed after them, as in the read)
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + NT - 1) / NT;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restr
   __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];
   uint4 a[ALDS ? 1 : R / 32];
   if constexpr (ALDS) {
-    load_a_lds<A_REGION>(w_up, lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave), lane, c0);
+    if (NT == 192 || wave < 3) load_a_lds<A_REGION>(w_up, lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave), lane, c0);
     vm_wait<0>();
 #pragma unroll
     for (int n = 0; n < NI; ++n)
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void cal_slab_down(const uint16_t* __restrict_
 // the up grid of the read (hc_up_mfma's lanes and W_up tile) loading lo, T x R floats, instead of 4 partials
 template <int T>
 __global__ __launch_bounds__(256) void cal_slab_up(const uint16_t* __restrict__ w_up, const char* scratch) {
-  constexpr int NT = upm_threads(T < 2 ? 2 : T);
+  constexpr int NT = upm_threads(T < 2 ? 2 : T, FMT_BF16);
   const float* lo = reinterpret_cast<const float*>(scratch + SLAB_OFF_LO);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;
@@ -333,7 +333,7 @@ extern "C" int hcrc_read_floor(int kind, int T, const void* w_down, const void* 
       return HCR_EALIGN;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const unsigned up_threads = T >= UP_MFMA_FROM ? upm_threads(T) : UP_THREADS;
+  const unsigned up_threads = T >= UP_MFMA_FROM ? upm_threads(T, FMT_BF16) : UP_THREADS;
   (void)hipGetLastError();
   if (kind == HCRC_EMPTY) {
     hipLaunchKernelGGL(cal_empty, dim3(DOWN_WGS), dim3(down_threads(T)), 0, st);
@@ -364,7 +364,7 @@ extern "C" int hcrc_up_kernel(int kind, int T, const void* w_up, void* scratch, 
     hipLaunchKernelGGL(kUpValu[T - 1], dim3(UP_WGS), dim3(UP_THREADS), 0, reinterpret_cast<hipStream_t>(stream), w_up,
                        nullptr, part, nullptr, nullptr, out, mean, lo);
   else
-    hipLaunchKernelGGL(kUpMfma[T - 1], dim3(UP_WGS), dim3(upm_threads(T)), 0, reinterpret_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(kUpMfma[T - 1], dim3(UP_WGS), dim3(upm_threads(T, FMT_BF16)), 0, reinterpret_cast<hipStream_t>(stream),
                        w_up, nullptr, part, nullptr, nullptr, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }
@@ -383,7 +383,7 @@ extern "C" int hcrc_slab_pair(int kind, int T, const void* w_down, const void* w
   (void)hipGetLastError();
   hipLaunchKernelGGL(kSlabDown[kind][T - 1], dim3(SLABS * SLAB_GROUPS), dim3(256), 0, st,
                      static_cast<const uint16_t*>(w_down), x, w_norm, sc);
-  hipLaunchKernelGGL(kSlabUp[T - 1], dim3(UP_WGS), dim3(upm_threads(T < 2 ? 2 : T)), 0, st,
+  hipLaunchKernelGGL(kSlabUp[T - 1], dim3(UP_WGS), dim3(upm_threads(T < 2 ? 2 : T, FMT_BF16)), 0, st,
                      static_cast<const uint16_t*>(w_up), static_cast<const char*>(sc));
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }

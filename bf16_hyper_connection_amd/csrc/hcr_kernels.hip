@@ -441,7 +441,7 @@ int launch_read(int fmt, int T, const void* w_down, const uint16_t* s_down, cons
   const bool mfma = T >= (fmt == FMT_BF16 ? UP_MFMA_FROM : UP_MFMA_FROM_Q8);
   const up_fn up = mfma ? kUpM[fmt][T - 1][inj != nullptr][pending != nullptr]
                         : kUp[fmt][T - 1][inj != nullptr][pending != nullptr];
-  hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(mfma ? upm_threads(T) : UP_THREADS), 0, st, w_up, s_up, part, inj,
+  hipLaunchKernelGGL(up, dim3(UP_WGS), dim3(mfma ? upm_threads(T, fmt) : UP_THREADS), 0, st, w_up, s_up, part, inj,
                      pending, out, mean, lo);
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }

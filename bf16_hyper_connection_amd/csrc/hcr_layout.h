@@ -57,9 +57,6 @@ constexpr int UP_WAVE_ROWS = UP_ROWS / (UP_THREADS / 64);    // 10
 constexpr int UP_ITERS = UP_WAVE_ROWS / 2;                   // 5 (two rows per iteration, one per half-wave)
 constexpr int UP_MFMA_FROM = 1;  // BF16 up projection on the matrix cores at every T (measured faster at T = 1 too)
 constexpr int UP_MFMA_FROM_Q8 = 4;  // the same for Q8_0 copies (their codes are widened per K step)
-// matrix-core up kernel: one 16-row tile of the 40 rows per wave (3 waves); from T = 10 a 4th wave (no tile)
-// halves the rounds of the lo staging, measured faster there
-constexpr int upm_threads(int T) { return T < 10 ? 192 : 256; }
 
 // ---- scratch (bytes) ----
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -96,6 +93,19 @@ static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0,
 
 // ---- weight formats: BF16, or Q8_0 copies (int8 codes + one binary16 scale per 32 weights of a row)
 enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
+
+// matrix-core up kernel: one 16-row tile of the 40 rows per wave (3 waves), plus a 4th wave with no tile when it
+// takes a round off the lo staging (T * R / 4 items, one per thread and round).  BF16 from T = 10, and below
+// where it saves a round (T = 3, 5, 6, 8, 9; its weights go straight into LDS, so the 4th wave loads none):
+// measured 0.17 us faster per read at T = 8 and 0.02-0.03 at T = 3, 5, 6; at T = 4 and 7, where the rounds stay
+// the same, 0.15 and 0.22 us slower.  Q8_0 copies from T = 10 (its 4th wave re-loads the third tile's codes).
+constexpr int staging_rounds(int T, int threads) { return (T * (R / 4) + threads - 1) / threads; }
+constexpr int upm_threads(int T, int fmt) {
+  return T >= 10 || (fmt == FMT_BF16 && staging_rounds(T, 256) < staging_rounds(T, 192)) ? 256 : 192;
+}
+static_assert(upm_threads(3, FMT_BF16) == 256 && upm_threads(4, FMT_BF16) == 192 && upm_threads(7, FMT_BF16) == 192 &&
+                  upm_threads(8, FMT_BF16) == 256 && upm_threads(9, FMT_Q8_0) == 192,
+              "the 4th wave where it saves a staging round");
 constexpr int Q8_BLOCK = 32;
 static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % down_ca(1) == 0 &&
                   Q8_BLOCK % down_ca(TMAX) == 0 && Q8_BLOCK % 8 == 0,

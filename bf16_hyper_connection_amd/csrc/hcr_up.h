@@ -259,7 +259,8 @@ __device__ __forceinline__ void load_a_lds(const uint16_t* __restrict__ w_up, ui
 
 // up on the matrix cores (BF16 weights from T = UP_MFMA_FROM, Q8_0 copies from T = UP_MFMA_FROM_Q8).  The
 // same work-group tile as hc_up (10 columns x 4 streams = 40 rows of W_up), as 3 tiles of 16 rows (waves
-// 0..2; rows 40..47 repeat row 39 and are not stored) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K
+// 0..2; rows 40..47 repeat rows 32..39 and are not stored; a 4th wave, where upm_threads gives one, only
+// stages lo) times v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 K
 // of W_up, B = 32 K x 16 columns
 // of lo split into BF16 high and low parts.  T <= 8: column t holds token t's high parts and column
 // 8 + t its low parts (one MFMA per K step); T > 8: one B matrix of high parts and one of low parts
@@ -271,7 +272,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
                                                   const float* __restrict__ part, const float* __restrict__ inj,
                                                   const float* pending, float* out, float* __restrict__ mean,
                                                   float* __restrict__ lo_out) {
-  constexpr int UPM_THREADS = upm_threads(T);
+  constexpr int UPM_THREADS = upm_threads(T, FMT);
   static_assert(T <= 16 && R % 32 == 0 && UP_ROWS > 32 && UP_ROWS <= 48 && (UPM_THREADS == 192 || UPM_THREADS == 256),
                 "3 tiles of 16 rows (waves 0..2), 16 token columns");
   static_assert(Q8_BLOCK == 32 && (R / Q8_BLOCK) % 2 == 0, "one Q8_0 block per MFMA K step; scale rows of whole dwords");
@@ -281,10 +282,12 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const int li = lane & 15, lg = lane >> 4;
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
   //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes
-  //    BF16 with 3 waves (T < 10, ALDS): every load of the kernel is untracked (ld*_untracked: the weights
-  //    go straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.
+  //    BF16 below T = 10 (ALDS): every load of the kernel is untracked (ld*_untracked: the weights go
+  //    straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.  A 4th wave (upm_threads:
+  //    where it takes a round off the staging) has no tile: with ALDS it loads no weights.
   constexpr bool NTW = UPM_THREADS == 192;
-  constexpr bool ALDS = !Q8 && NTW;
+  constexpr bool ALDS = !Q8 && T < 10;
+  constexpr bool WAVE4 = UPM_THREADS == 256;  // a 4th wave: no tile, it stages lo only
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
@@ -329,7 +332,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   //    2 p + 1 at 128 modulo 256: the read-back of one chunk's 16 rows meets 16 distinct LDS bank groups.  The
   //    third tile's rows 40..47 load rows 32..39 again (their products are not stored).
   //    Otherwise in the operand layout, into registers: lane (li, lg) loads row rw, K 32 m + 8 lg.  No load
-  //    is conditional: rows 40..47 of the third tile re-load row 39, and a 4th wave (T >= 10) re-loads the
+  //    is conditional: rows 40..47 of the third tile re-load row 39, and a 4th wave re-loads the
   //    third tile's rows, cache hits whose results are never stored (a branch around loads, even a
   //    wave-uniform one, makes the compiler wait for them before the first barrier).  Non-temporal, except
   //    with a 4th wave: its repeats of the third tile's rows are separate load instructions, which then
@@ -340,8 +343,9 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   uint4 a[ALDS || Q8 ? 1 : R / 32];  // BF16 in registers: 8 weights per step
   uint2 qa[Q8 ? R / 32 : 1];         // Q8_0: 8 codes per step
   if constexpr (ALDS) {
-    load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
-                         lane, c0);
+    if (!WAVE4 || wave < 3)
+      load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
+                           lane, c0);
   } else {
     const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
     const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
@@ -356,7 +360,10 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (ALDS) {  // the partials (and injection): all but the pending loads and the 10 weight loads
-    vm_wait<(PEND ? S : 0) + 10>();
+    if (!WAVE4 || wave < 3)
+      vm_wait<(PEND ? S : 0) + 10>();
+    else
+      vm_wait<PEND ? S : 0>();  // the 4th wave loads no weights
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
 #pragma unroll
