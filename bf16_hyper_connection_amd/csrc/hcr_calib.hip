@@ -116,7 +116,7 @@ __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t
 // straight into LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads none);
 // from T = 10 into registers in the operand layout (10 K steps).
 template <int T>
-__global__ __launch_bounds__(256) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
+__global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
                                                          const float* __restrict__ part) {
   constexpr int NT = upm_threads(T, FMT_BF16);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void cal_slab_down(const uint16_t* __restrict_
 
 // the up grid of the read (hc_up_mfma's lanes and W_up tile) loading lo, T x R floats, instead of 4 partials
 template <int T>
-__global__ __launch_bounds__(256) void cal_slab_up(const uint16_t* __restrict__ w_up, const char* scratch) {
+__global__ __launch_bounds__(upm_threads(T < 2 ? 2 : T, FMT_BF16)) void cal_slab_up(const uint16_t* __restrict__ w_up, const char* scratch) {
   constexpr int NT = upm_threads(T < 2 ? 2 : T, FMT_BF16);
   const float* lo = reinterpret_cast<const float*>(scratch + SLAB_OFF_LO);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(UP_THREADS) void cal_up_valu(const void* w_up, cons
   hc_up_body<T, false, false, FMT_BF16>(w_up, s_up, part, inj, pending, out, mean, lo_out);
 }
 template <int T>
-__global__ __launch_bounds__(256) void cal_up_mfma(const void* w_up, const uint16_t* s_up, const float* part,
+__global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma(const void* w_up, const uint16_t* s_up, const float* part,
                                                    const float* inj, const float* pending, float* out, float* mean,
                                                    float* lo_out) {
   hc_up_mfma_body<T, false, false, FMT_BF16>(w_up, s_up, part, inj, pending, out, mean, lo_out);

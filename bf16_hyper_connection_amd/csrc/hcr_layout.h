@@ -98,7 +98,9 @@ enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
 // takes a round off the lo staging (T * R / 4 items, one per thread and round).  BF16 from T = 10, and below
 // where it saves a round (T = 3, 5, 6, 8, 9; its weights go straight into LDS, so the 4th wave loads none):
 // measured 0.17 us faster per read at T = 8 and 0.02-0.03 at T = 3, 5, 6; at T = 4 and 7, where the rounds stay
-// the same, 0.15 and 0.22 us slower.  Q8_0 copies from T = 10 (its 4th wave re-loads the third tile's codes).
+// the same, 0.15 and 0.22 us slower.  More staging waves, although they take further rounds off, were slower:
+// 5 waves at T = 7 / 8 by 0.65 / 0.39 us, 8 waves at T = 6 by 0.63 us.  Q8_0 copies from T = 10 (its 4th wave
+// re-loads the third tile's codes).
 constexpr int staging_rounds(int T, int threads) { return (T * (R / 4) + threads - 1) / threads; }
 constexpr int upm_threads(int T, int fmt) {
   return T >= 10 || (fmt == FMT_BF16 && staging_rounds(T, 256) < staging_rounds(T, 192)) ? 256 : 192;

@@ -273,8 +273,9 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
                                                   const float* pending, float* out, float* __restrict__ mean,
                                                   float* __restrict__ lo_out) {
   constexpr int UPM_THREADS = upm_threads(T, FMT);
-  static_assert(T <= 16 && R % 32 == 0 && UP_ROWS > 32 && UP_ROWS <= 48 && (UPM_THREADS == 192 || UPM_THREADS == 256),
-                "3 tiles of 16 rows (waves 0..2), 16 token columns");
+  static_assert(T <= 16 && R % 32 == 0 && UP_ROWS > 32 && UP_ROWS <= 48 && UPM_THREADS % 64 == 0 && UPM_THREADS >= 192 &&
+                    UPM_THREADS <= 512,
+                "3 tiles of 16 rows (waves 0..2; further waves stage lo only), 16 token columns");
   static_assert(Q8_BLOCK == 32 && (R / Q8_BLOCK) % 2 == 0, "one Q8_0 block per MFMA K step; scale rows of whole dwords");
   constexpr bool Q8 = FMT == FMT_Q8_0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -287,7 +288,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   //    where it takes a round off the staging) has no tile: with ALDS it loads no weights.
   constexpr bool NTW = UPM_THREADS == 192;
   constexpr bool ALDS = !Q8 && T < 10;
-  constexpr bool WAVE4 = UPM_THREADS == 256;  // a 4th wave: no tile, it stages lo only
+  constexpr bool EXTRA = UPM_THREADS > 192;  // waves beyond the 3 tiles: no tile, they stage lo only
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
@@ -343,7 +344,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   uint4 a[ALDS || Q8 ? 1 : R / 32];  // BF16 in registers: 8 weights per step
   uint2 qa[Q8 ? R / 32 : 1];         // Q8_0: 8 codes per step
   if constexpr (ALDS) {
-    if (!WAVE4 || wave < 3)
+    if (!EXTRA || wave < 3)
       load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
                            lane, c0);
   } else {
@@ -360,10 +361,10 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (ALDS) {  // the partials (and injection): all but the pending loads and the 10 weight loads
-    if (!WAVE4 || wave < 3)
+    if (!EXTRA || wave < 3)
       vm_wait<(PEND ? S : 0) + 10>();
     else
-      vm_wait<PEND ? S : 0>();  // the 4th wave loads no weights
+      vm_wait<PEND ? S : 0>();  // a wave with no tile loads no weights
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
 #pragma unroll
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(UP_THREADS) void hc_up(const void* __restrict__ w_u
   hc_up_body<T, INJ, PEND, FMT>(w_up, s_up, part, inj, pending, out, mean, lo_out);
 }
 template <int T, bool INJ, bool PEND, int FMT>
-__global__ __launch_bounds__(256) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
+__global__ __launch_bounds__(upm_threads(T, FMT)) void hc_up_mfma(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
                                                   const float* __restrict__ part, const float* __restrict__ inj,
                                                   const float* pending, float* out, float* __restrict__ mean,
                                                   float* __restrict__ lo_out) {
