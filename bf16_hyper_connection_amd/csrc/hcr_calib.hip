@@ -112,9 +112,9 @@ __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t
   }
 }
 
-// hc_up_mfma<T>'s loads: partials, then one 16-row tile of W_up per wave.  Below T = 10 the weights go
-// straight into LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads none);
-// from T = 10 into registers in the operand layout (10 K steps).
+// hc_up_mfma<T>'s loads: partials, then one 16-row tile of W_up per wave.  Up to T = 12 (up_weights_lds) the
+// weights go straight into LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads
+// none); from T = 13 into registers in the operand layout (10 K steps).
 template <int T>
 __global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
                                                          const float* __restrict__ part) {
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(co
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;
   const int li = lane & 15, lg = lane >> 4;
-  constexpr bool ALDS = T < 10;
+  constexpr bool ALDS = up_weights_lds(T, FMT_BF16);
   // the partials first (issued before the weights, consumed after them, as in the read)
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + NT - 1) / NT;

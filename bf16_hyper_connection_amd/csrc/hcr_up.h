@@ -283,11 +283,12 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const int li = lane & 15, lg = lane >> 4;
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
   //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes
-  //    BF16 below T = 10 (ALDS): every load of the kernel is untracked (ld*_untracked: the weights go
-  //    straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.  A 4th wave (upm_threads:
-  //    where it takes a round off the staging) has no tile: with ALDS it loads no weights.
+  //    BF16 up to T = 12 (ALDS, up_weights_lds): every load of the kernel is untracked (ld*_untracked: the
+  //    weights go straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.  A 4th wave
+  //    (upm_threads: from T = 10, and below where it takes a round off the staging) has no tile: with ALDS it
+  //    loads no weights.
   constexpr bool NTW = UPM_THREADS == 192;
-  constexpr bool ALDS = !Q8 && T < 10;
+  constexpr bool ALDS = up_weights_lds(T, FMT);
   constexpr bool EXTRA = UPM_THREADS > 192;  // waves beyond the 3 tiles: no tile, they stage lo only
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
@@ -337,7 +338,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   //    third tile's rows, cache hits whose results are never stored (a branch around loads, even a
   //    wave-uniform one, makes the compiler wait for them before the first barrier).  Non-temporal, except
   //    with a 4th wave: its repeats of the third tile's rows are separate load instructions, which then
-  //    missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16).
+  //    missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16, before T = 10..12 took the LDS path).
   constexpr int A_REGION = 10 * A_LOAD_STRIDE;
   static_assert(R == 320, "5 lines of 128 bytes per BF16 row, 10 loads per wave");
   __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];

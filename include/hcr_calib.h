@@ -16,7 +16,7 @@
  *               the same cache policy (down: the stream's x for the T tokens,
  *               w_norm, then the work-group's 5 rows of W_down; up: the 4 stream
  *               partials of lo, then the work-group's 40 rows of W_up, for
- *               T = 2..9 straight into LDS as the read loads them), wait for
+ *               T = 1..12 straight into LDS as the read loads them), wait for
  *               every loaded value and discard it: no arithmetic, no other LDS
  *               access, no barrier, no store.
  *
