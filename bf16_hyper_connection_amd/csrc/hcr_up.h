@@ -294,13 +294,22 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   constexpr int NI = (ITEMS + UPM_THREADS - 1) / UPM_THREADS;
   f32x4 pv[NI][S], iv[NI];
   if constexpr (ALDS) {
+    static_assert(!ALDS || UPM_THREADS <= 256, "at most one staging-only wave on the LDS path");
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int n = 0; n < NI; ++n) {  // load_partials' items and order
       const int it = min(tid + n * UPM_THREADS, ITEMS - 1);
       const int t = it / (R / 4), k = 4 * (it % (R / 4));
+      // The staging-only 4th wave skips a round whose items all lie past the end (T = 5, 8, 10..12), where
+      // it would load the last item 4 times over for nothing (its wait counts only the younger pending loads,
+      // so it stays exact).  Measured on MI355X (bench.py --ab, one process, alternating builds, 5 rounds):
+      // 0.17 us faster per read at T = 8, level at the other T.  The tile waves keep their repeats: skipping
+      // them as well (whole waves, or lane by lane) was 0.05-0.2 us slower at T = 1, 2, 4 and 10..11
+      if (!(EXTRA && 192 + n * UPM_THREADS >= ITEMS && wv >= 3)) {
 #pragma unroll
-      for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
-      if (INJ) iv[n] = ld4_untracked(inj + (size_t)t * R + k);
+        for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
+        if (INJ) iv[n] = ld4_untracked(inj + (size_t)t * R + k);
+      }
     }
   } else {
     load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
