@@ -210,6 +210,62 @@ def ab_compare(args, readers, xs, outs, means, stream, timed):
     return res
 
 
+def ab_window(args, stream, timed):
+    """The 96-read verify window (the bench's own workload: residual chain, T = 6, pending on, distinct weight
+    sets) through several builds of libhcr.so, alternating round by round in one process; median µs per window
+    and per read for each build."""
+    import ctypes
+    import torch
+    from bf16_hyper_connection_amd import inputs as gen
+    dev = torch.device("cuda:0")
+    n_win, t_win = 96, 6
+    cw = gen.verify_window(n_win, t_win)
+    wts = [(torch.from_numpy(w.w_down.view(np.int16)).to(dev), torch.from_numpy(w.w_up.view(np.int16)).to(dev),
+            torch.from_numpy(w.w_norm).to(dev)) for w in cw["weights"]]
+    del cw["weights"]
+    wpend = [torch.from_numpy(p_).to(dev) for p_ in cw["pending"]]
+    wx0 = torch.from_numpy(cw["x0"]).to(dev)
+    wouts = [torch.empty((t_win, S, D), device=dev) for _ in range(n_win)]
+    wmeans = [torch.empty((t_win, D), device=dev) for _ in range(n_win)]
+    vp = ctypes.c_void_p
+    libs = []
+    for path in args.ab:
+        L = ctypes.CDLL(os.path.abspath(path), mode=os.RTLD_LOCAL)
+        L.hcr_scratch_bytes.restype, L.hcr_scratch_bytes.argtypes = ctypes.c_size_t, []
+        L.hcr_create.restype, L.hcr_create.argtypes = ctypes.c_int, [vp, vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.hcr_read.restype, L.hcr_read.argtypes = ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+        nb = L.hcr_scratch_bytes()
+        handles, scratch = [], []
+        for wd, wu, wn in wts:
+            sc = torch.empty(nb, dtype=torch.uint8, device=dev)
+            h = vp()
+            rc = L.hcr_create(wd.data_ptr(), wu.data_ptr(), wn.data_ptr(), sc.data_ptr(), nb, ctypes.byref(h))
+            assert rc == 0, (path, rc)
+            handles.append(h)
+            scratch.append(sc)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                xx = wx0
+                for i, h in enumerate(handles):
+                    rc = L.hcr_read(h, t_win, xx.data_ptr(), wpend[i].data_ptr(), None, wouts[i].data_ptr(),
+                                    wmeans[i].data_ptr(), vp(stream.cuda_stream))
+                    assert rc == 0, (path, rc)
+                    xx = wouts[i]
+        torch.cuda.current_stream().wait_stream(stream)
+        libs.append((os.path.basename(path), L, handles, scratch, g))
+    reps = 20
+    times = {name: [] for name, *_ in libs}
+    for rnd in range(args.ab_rounds):
+        for name, L, handles, scratch, g in libs:
+            times[name].append(timed(g, reps, 2) * 1000.0 / reps)
+            log(f"bench: A/B window round {rnd} {name}: {times[name][-1]:.2f} us")
+    return {name: {"us_per_window": round(float(np.median(v)), 2), "us_per_read": round(float(np.median(v)) / n_win, 3),
+                   "spread_us": round(max(v) - min(v), 2)} for name, v in times.items()}
+
+
 def sha256_of(*tensors):
     """sha256 (hex) of the bytes of device tensors, in order."""
     import hashlib
@@ -239,6 +295,9 @@ def main():
     ap.add_argument("--ab-rounds", type=int, default=3)
     ap.add_argument("--ab-tmax", type=int, default=8, help="A/B mode: T = 1..this")
     ap.add_argument("--ab-q8", action="store_true", help="A/B mode: read Q8_0 copies (each build quantises)")
+    ap.add_argument("--ab-window", action="store_true",
+                    help="A/B mode: time the 96-read verify window (T = 6, pending on, residual chain) through "
+                         "each build instead of the per-T sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 64 MiB device copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -303,6 +362,12 @@ def main():
             torch.cuda.synchronize()
         return e0.elapsed_time(e1)  # ms
 
+    if args.ab and args.ab_window:
+        res = ab_window(args, stream, timed)
+        print(json.dumps({"ab_window": res, "rounds": args.ab_rounds,
+                          "note": "median µs per 96-read verify window over the rounds, libraries alternating"}),
+              flush=True)
+        return
     if args.ab:
         res = ab_compare(args, readers, xs, outs, means, stream, timed)
         print(json.dumps({"ab": res, "rounds": args.ab_rounds, "weight_sets": len(readers),

@@ -325,11 +325,22 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   // pending loads are clamped to a valid (token, column), so that no branch separates the loads
   const int cc = 4 * wave + lg;
   const bool eok = wave < 3 && cc < UP_COLS && li < T;
+  // A staging-only 4th wave on the LDS path has no epilogue lanes and loads no pending values (its loads are
+  // untracked, so the branch adds no wait).  Measured on MI355X (bench.py --ab --ab-window, one process,
+  // alternating builds, 6 rounds): the 96-read window (T = 6, pending on) from 721.3 to 712.6 us; skipping the
+  // tile waves' lanes outside the epilogue as well gave 715.3 us
   float pend[S];
+  const bool pload = !(ALDS && EXTRA) || __builtin_amdgcn_readfirstlane(wave) < 3;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const float* pp = pending + ((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1);
-    pend[s] = !PEND ? 0.f : ALDS ? ld1_untracked(pp) : *pp;
+    pend[s] = 0.f;
+    if (PEND) {
+      if (!ALDS)
+        pend[s] = *pp;
+      else if (pload)
+        pend[s] = ld1_untracked(pp);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keeps every small load ahead of the weight loads
   // 2. weights (A operand), tile = wave: row rw = 16 * wave + li of the work-group's 40 (rw & 3 = stream,
@@ -374,7 +385,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     if (!EXTRA || wave < 3)
       vm_wait<(PEND ? S : 0) + 10>();
     else
-      vm_wait<PEND ? S : 0>();  // a wave with no tile loads no weights
+      vm_wait<0>();  // a wave with no tile loads no weights, and no pending values
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
 #pragma unroll
