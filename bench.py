@@ -456,6 +456,25 @@ def main():
                 calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
                 del gk
             log(f"bench: calibration {key}: {calibration[key]}")
+        # the whole read in the pages' shape, with its arithmetic (hcrc_slab_read: slab down kernel, last-arriver
+        # finish writing lo and rs, the read's up kernel on lo), the sweep's x, T = 1..8, beside per_T_us
+        cal.hcrc_slab_read.restype = ctypes.c_int
+        cal.hcrc_slab_read.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 10
+        calibration["slab_read_us"] = {}
+        for T in range(1, TMAX + 1):
+            gk = torch.cuda.CUDAGraph()
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(gk, stream=stream):
+                    for r in readers:
+                        rc = cal.hcrc_slab_read(T, r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(),
+                                                slab_sc.data_ptr(), xs[T].data_ptr(), None, None, outs[T].data_ptr(),
+                                                means[T].data_ptr(), stream.cuda_stream)
+                        assert rc == hcr.HCR_OK, rc
+            torch.cuda.current_stream().wait_stream(stream)
+            calibration["slab_read_us"][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+            del gk
+        log(f"bench: calibration slab_read_us: {calibration['slab_read_us']}")
         del slab_sc
         calibration["read_over_loads_us"] = {T: round(per_T_us[T] - calibration["loads_pair_us"][T], 3)
                                              for T in range(1, T_WIDE + 1)}
@@ -484,7 +503,9 @@ def main():
                                "arithmetic, LDS, barrier or store); loads_store_pair = loads_pair with one store per down "
                                "work-group; read_over_loads = per_T_us - loads_pair; slab_* = the pages' 10-row x "
                                "1,280-column down shape: its loads (up kernel loading lo only), + its partial stores, "
-                               "+ the last-arriver finish (agent-scope acquire-release counter); "
+                               "+ the last-arriver finish (agent-scope acquire-release counter); slab_read = the whole read in "
+                               "that shape with its arithmetic (slab partials, the finish applying rs and writing lo, "
+                               "the read's up kernel on lo), µs per read beside per_T_us; "
                                "up_valu / up_mfma = the read's two up kernels alone, µs per launch")
 
     # the full epilogue (pending write and injection on) over the same 32 rotated weight sets: T = 4 with the

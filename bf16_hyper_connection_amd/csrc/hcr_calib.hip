@@ -261,6 +261,147 @@ __global__ __launch_bounds__(upm_threads(T < 2 ? 2 : T, FMT_BF16)) void cal_slab
   for (int m = 0; m < R / 32; ++m) use(a[m]);
 }
 
+// ---- the pages' read with its arithmetic (hcrc_slab_read): the slab down kernel computes a = x * w_norm
+// (unscaled), the slab's sums of squares and its 10 rows' partials; the last work-group of a row group to
+// arrive applies rs per stream, adds the injection, writes lo (and rs) and resets the counter; the read's own
+// up kernel then reads lo alone (NSRC = 1).  Scratch: the slab layout above, plus rs [TMAX][S] and a region
+// that takes the up kernel's copy of lo (unused here).
+constexpr size_t SLAB_OFF_RS = SLAB_OFF_LO + size_t(TMAX) * R * 4;
+constexpr size_t SLAB_OFF_JUNK = SLAB_OFF_RS + size_t(TMAX) * S * 4;
+static_assert(SLAB_OFF_JUNK + size_t(TMAX) * R * 4 <= HCRC_SLAB_SCRATCH_BYTES && SLAB_OFF_LO == HCRC_SLAB_OFF_LO &&
+                  SLAB_OFF_RS == HCRC_SLAB_OFF_RS,
+              "the slab scratch holds the read too, at the offsets the header states");
+
+template <int T, bool INJ>
+__global__ __launch_bounds__(256) void cal_slab_read_down(const uint16_t* __restrict__ w_down, const float* __restrict__ x,
+                                                          const float* __restrict__ w_norm, const float* __restrict__ inj,
+                                                          char* scratch) {
+  const int b = blockIdx.x;
+  const int sl = (b / XCDS) % SLABS, g = b % XCDS + XCDS * (b / (XCDS * SLABS));  // as cal_slab_down
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ca = sl * SLAB_COLS + 256 * wave + 4 * lane, cb = sl * SLAB_COLS + 1024 + 64 * wave + lane;
+  float* part = reinterpret_cast<float*>(scratch);
+  float* ssb = reinterpret_cast<float*>(scratch + SLAB_OFF_SS);
+  unsigned* ctr = reinterpret_cast<unsigned*>(scratch + SLAB_OFF_CTR);
+  float* lo = reinterpret_cast<float*>(scratch + SLAB_OFF_LO);
+  float* rs_out = reinterpret_cast<float*>(scratch + SLAB_OFF_RS);
+  // loads: x of the T tokens and w_norm at the lane's 4 + 1 columns, then the 10 weight rows
+  f32x4 xa[T];
+  float xb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    xa[t] = ld4(x + (size_t)t * DD + ca);
+    xb[t] = x[(size_t)t * DD + cb];
+  }
+  const f32x4 na = ld4(w_norm + ca);
+  const float nb = w_norm[cb];
+  uint2 wa[SLAB_ROWS];
+  uint32_t wb[SLAB_ROWS];
+#pragma unroll
+  for (int r = 0; r < SLAB_ROWS; ++r) {
+    wa[r] = ldw8(w_down + (size_t)(SLAB_ROWS * g + r) * DD + ca);
+    wb[r] = ldw2(w_down + (size_t)(SLAB_ROWS * g + r) * DD + cb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the lane's values: the T sums of squares (value t), then row r, token t (value T + r T + t)
+  constexpr int NV = (SLAB_ROWS + 1) * T, N = round4(NV);
+  float v[N];
+#pragma unroll
+  for (int k = NV; k < N; ++k) v[k] = 0.f;
+  float act[T][5];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      act[t][e] = xa[t][e] * na[e];
+      ss = __builtin_fmaf(xa[t][e], xa[t][e], ss);
+    }
+    act[t][4] = xb[t] * nb;
+    v[t] = __builtin_fmaf(xb[t], xb[t], ss);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < SLAB_ROWS; ++r) {
+    const float wv[5] = {__uint_as_float(wa[r].x << 16), __uint_as_float(wa[r].x & 0xffff0000u),
+                         __uint_as_float(wa[r].y << 16), __uint_as_float(wa[r].y & 0xffff0000u),
+                         __uint_as_float(wb[r] << 16)};
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 5; ++e) acc = __builtin_fmaf(wv[e], act[t][e], acc);
+      v[T + r * T + t] = acc;
+    }
+  }
+  // sums over the wave, then over the 4 waves in a fixed order; the slab's unscaled partials and its sums
+  // of squares go to the scratch
+  wave_sum<N>(v);
+  __shared__ float wsum[4][N];
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) wsum[wave][(lane >> 4) * (N / 4) + i] = v[i];
+  }
+  __syncthreads();
+  if (tid < NV) {
+    const float a = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+    if (tid < T)
+      ssb[sl * TMAX + tid] = a;
+    else
+      part[((size_t)sl * TMAX + (tid - T) % T) * R + SLAB_ROWS * g + (tid - T) / T] = a;
+  }
+  // the finish: one agent-scope acquire-release arrival per work-group (every thread's stores precede it
+  // through the barrier); the 8th work-group of the row group reads the 8 slabs, nobody waits
+  __shared__ int last;
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(ctr + g, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == SLABS - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  // rs[t][s] = 1 / sqrt((ss of the stream's 2 slabs) / D + 1e-6); lo[t][r] = sum_s rs * (its 2 slab partials)
+  // (+ inj), streams in order
+  if (tid < SLAB_ROWS * T) {
+    const int t = tid / SLAB_ROWS, r = SLAB_ROWS * g + tid % SLAB_ROWS;
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float ms = (ssb[(2 * s) * TMAX + t] + ssb[(2 * s + 1) * TMAX + t]) * (1.0f / D);
+      const float rs = 1.0f / sqrtf(ms + 1e-6f);
+      acc = __builtin_fmaf(rs, part[((size_t)(2 * s) * TMAX + t) * R + r] + part[((size_t)(2 * s + 1) * TMAX + t) * R + r], acc);
+    }
+    if (INJ) acc += inj[(size_t)t * R + r];
+    lo[(size_t)t * R + r] = acc;
+  }
+  if (g == 0 && tid < S * T) {
+    const int t = tid / S, s = tid % S;
+    const float ms = (ssb[(2 * s) * TMAX + t] + ssb[(2 * s + 1) * TMAX + t]) * (1.0f / D);
+    rs_out[t * S + s] = 1.0f / sqrtf(ms + 1e-6f);
+  }
+  if (tid == 0) __hip_atomic_store(ctr + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the read's up kernel on lo alone (its staging reads one source: NSRC = 1); the injection is already in lo
+template <int T, bool PEND>
+__global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_slab_read_up(const void* w_up, const float* lo,
+                                                                             const float* pending, float* out,
+                                                                             float* mean, float* junk) {
+  hc_up_mfma_body<T, false, PEND, FMT_BF16, 1>(w_up, nullptr, lo, nullptr, pending, out, mean, junk);
+}
+
+typedef void (*slab_read_down_fn)(const uint16_t*, const float*, const float*, const float*, char*);
+typedef void (*slab_read_up_fn)(const void*, const float*, const float*, float*, float*, float*);
+#define HCRC_SRD(T) {cal_slab_read_down<T, false>, cal_slab_read_down<T, true>}
+const slab_read_down_fn kSlabReadDown[8][2] = {HCRC_SRD(1), HCRC_SRD(2), HCRC_SRD(3), HCRC_SRD(4),
+                                               HCRC_SRD(5), HCRC_SRD(6), HCRC_SRD(7), HCRC_SRD(8)};
+#undef HCRC_SRD
+#define HCRC_SRU(T) {cal_slab_read_up<T, false>, cal_slab_read_up<T, true>}
+const slab_read_up_fn kSlabReadUp[8][2] = {HCRC_SRU(1), HCRC_SRU(2), HCRC_SRU(3), HCRC_SRU(4),
+                                           HCRC_SRU(5), HCRC_SRU(6), HCRC_SRU(7), HCRC_SRU(8)};
+#undef HCRC_SRU
+
 typedef void (*slab_down_fn)(const uint16_t*, const float*, const float*, char*);
 typedef void (*slab_up_fn)(const uint16_t*, const char*);
 #define HCRC_SLAB_ROW(K) {cal_slab_down<1, K>, cal_slab_down<2, K>, cal_slab_down<3, K>, cal_slab_down<4, K>, \
@@ -385,5 +526,26 @@ extern "C" int hcrc_slab_pair(int kind, int T, const void* w_down, const void* w
                      static_cast<const uint16_t*>(w_down), x, w_norm, sc);
   hipLaunchKernelGGL(kSlabUp[T - 1], dim3(UP_WGS), dim3(upm_threads(T < 2 ? 2 : T, FMT_BF16)), 0, st,
                      static_cast<const uint16_t*>(w_up), static_cast<const char*>(sc));
+  return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
+}
+
+extern "C" int hcrc_slab_read(int T, const void* w_down, const void* w_up, const float* w_norm, void* slab_scratch,
+                              const float* x, const float* pending, const float* inj, float* out, float* mean,
+                              void* stream) {
+  using namespace hcr;
+  if (T < 1 || T > 8) return HCR_EINVAL;
+  if (!w_down || !w_up || !w_norm || !slab_scratch || !x || !out || !mean) return HCR_EINVAL;
+  if (!aligned(w_down, 16) || !aligned(w_up, 16) || !aligned(w_norm, 16) || !aligned(slab_scratch, 256) ||
+      !aligned(x, 16) || !aligned(out, 16) || !aligned(mean, 16) || (pending && !aligned(pending, 16)) ||
+      (inj && !aligned(inj, 16)))
+    return HCR_EALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* sc = static_cast<char*>(slab_scratch);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kSlabReadDown[T - 1][inj != nullptr], dim3(SLABS * SLAB_GROUPS), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w_down), x, w_norm, inj, sc);
+  hipLaunchKernelGGL(kSlabReadUp[T - 1][pending != nullptr], dim3(UP_WGS), dim3(upm_threads(T, FMT_BF16)), 0, st,
+                     w_up, reinterpret_cast<const float*>(sc + SLAB_OFF_LO), pending, out, mean,
+                     reinterpret_cast<float*>(sc + SLAB_OFF_JUNK));
   return hipGetLastError() == hipSuccess ? HCR_OK : HCR_EHIP;
 }

@@ -17,7 +17,7 @@ namespace hcr {
 // past the end load the last item again (store_lo puts those repeats in junk slots).  A branch among the loads
 // makes the compiler wait for every load issued so far, and a branch around their only use lets it sink
 // them below the weight loads; either would serialise them with the weight stream.
-template <int T, bool INJ, int NI, int NT>
+template <int T, bool INJ, int NI, int NT, int NSRC = S>
 __device__ __forceinline__ void load_partials(int tid, const float* __restrict__ part,
                                               const float* __restrict__ inj, f32x4 (&pv)[NI][S],
                                               f32x4 (&iv)[NI]) {
@@ -27,7 +27,7 @@ __device__ __forceinline__ void load_partials(int tid, const float* __restrict__
     const int it = min(tid + n * NT, ITEMS - 1);
     const int t = it / (R / 4), k = 4 * (it % (R / 4));
 #pragma unroll
-    for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
+    for (int ss = 0; ss < NSRC; ++ss) pv[n][ss] = ld4(part + ((size_t)ss * TMAX + t) * R + k);
     if (INJ) iv[n] = ld4(inj + (size_t)t * R + k);
   }
 }
@@ -266,8 +266,10 @@ __device__ __forceinline__ void load_a_lds(const uint16_t* __restrict__ w_up, ui
 // 8 + t its low parts (one MFMA per K step); T > 8: one B matrix of high parts and one of low parts
 // (two MFMAs per K step, high then low, into the same accumulator).  Lane (li, lg) then holds column li
 // of rows 4 lg .. 4 lg + 3 of its tile: the 4 streams of one output column, so the epilogue and the
-// stream mean stay in the lane (T <= 8: after adding column li + 8 by a row rotation).
-template <int T, bool INJ, bool PEND, int FMT>
+// stream mean stay in the lane (T <= 8: after adding column li + 8 by a row rotation).  NSRC: the number of
+// partial sources summed into lo, the 4 stream partials in the read; 1 where lo itself is given (the
+// calibration library's read in the pages' shape, whose down kernel finishes lo).
+template <int T, bool INJ, bool PEND, int FMT, int NSRC = S>
 __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, const uint16_t* __restrict__ s_up,
                                                   const float* __restrict__ part, const float* __restrict__ inj,
                                                   const float* pending, float* out, float* __restrict__ mean,
@@ -277,6 +279,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
                     UPM_THREADS <= 512,
                 "3 tiles of 16 rows (waves 0..2; further waves stage lo only), 16 token columns");
   static_assert(Q8_BLOCK == 32 && (R / Q8_BLOCK) % 2 == 0, "one Q8_0 block per MFMA K step; scale rows of whole dwords");
+  static_assert(NSRC == S || NSRC == 1, "lo from the 4 stream partials, or lo itself");
   constexpr bool Q8 = FMT == FMT_Q8_0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;  // an XCD's tiles are contiguous
@@ -307,12 +310,12 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
       // them as well (whole waves, or lane by lane) was 0.05-0.2 us slower at T = 1, 2, 4 and 10..11
       if (!(EXTRA && 192 + n * UPM_THREADS >= ITEMS && wv >= 3)) {
 #pragma unroll
-        for (int ss = 0; ss < S; ++ss) pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
+        for (int ss = 0; ss < NSRC; ++ss) pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
         if (INJ) iv[n] = ld4_untracked(inj + (size_t)t * R + k);
       }
     }
   } else {
-    load_partials<T, INJ, NI, UPM_THREADS>(tid, part, inj, pv, iv);
+    load_partials<T, INJ, NI, UPM_THREADS, NSRC>(tid, part, inj, pv, iv);
   }
   constexpr int NSC = Q8 ? (SC_WORDS + UPM_THREADS - 1) / UPM_THREADS : 0;
   uint32_t scw[NSC > 0 ? NSC : 1];
@@ -389,7 +392,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
 #pragma unroll
-      for (int ss = 0; ss < S; ++ss) vm_pin(pv[n][ss]);
+      for (int ss = 0; ss < NSRC; ++ss) vm_pin(pv[n][ss]);
       if (INJ) vm_pin(iv[n]);
     }
   }
@@ -414,7 +417,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   for (int n = 0; n < NI; ++n) {
     const int it0 = tid + n * UPM_THREADS, it = min(it0, ITEMS - 1);
     const int t = it / (R / 4), k = 4 * (it % (R / 4));
-    f32x4 vv = ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3];
+    f32x4 vv = NSRC == S ? ((pv[n][0] + pv[n][1]) + pv[n][2]) + pv[n][3] : pv[n][0];
     if (INJ) vv += iv[n];
     uint2 hi, lo;
     split_hi_lo4(vv, hi, lo);

@@ -102,6 +102,40 @@ enum { HCRC_SLAB_LOADS = 0, HCRC_SLAB_STORES = 1, HCRC_SLAB_FINISH = 2 };
 int hcrc_slab_pair(int kind, int T, const void* w_down, const void* w_up, const float* w_norm, void* slab_scratch,
                    const float* x, void* stream);
 
+/*
+ * hcrc_slab_read: the whole read in the pages' shape, with its arithmetic
+ * (Strata PR #2812, What changed: the down kernel stages x * w_norm unscaled
+ * with the slab's sums of squares; the last work-group of a row group to
+ * arrive applies rs per stream, writes lo, the injection and rs, and resets
+ * the counter; the up kernel reads lo).  Down: the work-groups, lanes and
+ * loads of hcrc_slab_pair, each computing its slab's T sums of squares and
+ * its 10 rows' unscaled partials (one FP32 FMA chain per row and token over
+ * the exactly widened weights, then the wave and the 4 waves in a fixed
+ * order), then one agent-scope acquire-release arrival; the 8th arrival of a
+ * row group computes rs[t][s] = 1 / sqrt(mean of squares + 1e-6) from the
+ * stream's two slabs, lo[t][r] = sum over s of rs * (its two slab partials),
+ * plus inj[t][r] when inj is given, writes lo (and, for row group 0, rs) and
+ * sets the counter back to zero; nobody waits.  Up: libhcr.so's up kernel
+ * (hc_up_mfma's body) reading lo alone instead of 4 stream partials, with the
+ * pending write when pending is given, then the gate and the stream mean.
+ * Results: out [T][4][2560] and mean [T][2560] as hcr_read's, within the
+ * same tolerance of the reference (the sums run in another order, so not
+ * bitwise hcr_read's); lo [T][320] and rs [T][4] at HCRC_SLAB_OFF_LO and
+ * HCRC_SLAB_OFF_RS bytes into slab_scratch.  Measurement only: it prices the
+ * pages' finish on MI355X with the arithmetic in place.
+ * slab_scratch: HCRC_SLAB_SCRATCH_BYTES bytes, 256-byte aligned, zero-filled
+ * before the first call (each call leaves its counters at zero), used by one
+ * stream at a time.  w_down, w_up (BF16), w_norm, x: as for hcrc_read_floor;
+ * pending [T][4][2560] and inj [T][320] fp32 may be NULL (off).  Every
+ * pointer 16-byte aligned.  T in 1..8.  out must not overlap x, pending or
+ * the scratch.  Errors: HCR_EINVAL, HCR_EALIGN (before any HIP call),
+ * HCR_EHIP.
+ */
+#define HCRC_SLAB_OFF_LO 164864u
+#define HCRC_SLAB_OFF_RS 185344u
+int hcrc_slab_read(int T, const void* w_down, const void* w_up, const float* w_norm, void* slab_scratch,
+                   const float* x, const float* pending, const float* inj, float* out, float* mean, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
