@@ -27,6 +27,10 @@ METRIC = "µs per cold HC read (norm+down+up) at T=1..8; achieved HBM GB/s vs pe
 HBM_PEAK_GBPS = 8000.0
 S, D, R, TMAX = 4, 2560, 320, 8
 T_WIDE = 16  # larger verify windows, reported per T beside the step
+# A graph replay costs ~6 us of its own on this stack (a graph of two 96-read windows takes 2 W + 6 us, one
+# window W + 6 us), so the per-T graphs pass ROT times over the rotated sets (256 reads each) and a replay
+# boundary adds ~0.02 us to a read instead of ~0.2 us with one pass of 32
+ROT = 8
 W_BYTES = 2 * R * S * D * 2
 
 
@@ -189,7 +193,7 @@ def ab_compare(args, readers, xs, outs, means, stream, timed):
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
                 with torch.cuda.graph(g, stream=stream):
-                    for h in handles:
+                    for h in handles * ROT:
                         rc = L.hcr_read(h, T, xs[T].data_ptr(), None, None, outs[T].data_ptr(), means[T].data_ptr(),
                                         vp(stream.cuda_stream))
                         assert rc == 0, (path, T, rc)
@@ -200,7 +204,7 @@ def ab_compare(args, readers, xs, outs, means, stream, timed):
     for rnd in range(args.ab_rounds):
         for name, L, handles, scratch, graphs in libs:
             for T in Ts:
-                times[name][T].append(timed(graphs[T], args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(handles)))
+                times[name][T].append(timed(graphs[T], args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(handles)))
             log(f"bench: A/B round {rnd} {name}: " + " ".join(f"{times[name][T][-1]:.3f}" for T in Ts))
     res = {}
     for name in times:
@@ -381,9 +385,9 @@ def main():
     per_T_us, per_T_gbps, hashes = {}, {}, {"cold_sweep": {}}
     replay_equals_direct = True
     for T in range(1, T_WIDE + 1):
-        g = capture([T], len(readers))
+        g = capture([T], ROT * len(readers))
         ms = timed(g, args.per_t_reps, 2)
-        us = ms * 1000.0 / (args.per_t_reps * len(readers))
+        us = ms * 1000.0 / (args.per_t_reps * ROT * len(readers))
         per_T_us[T] = round(us, 3)
         per_T_gbps[T] = round(algorithmic_bytes(T) / us / 1e3, 1)
         log(f"bench: T={T} {us:.3f} us/read  {per_T_gbps[T]:.0f} GB/s")
@@ -400,7 +404,8 @@ def main():
     cold_check = {}
     for T in (1, TMAX):
         row = {}
-        for name, pool in (("1_set", readers[:1] * len(readers)), ("32_sets", readers), ("64_sets", readers + extra)):
+        for name, pool in (("1_set", readers[:1] * (ROT * len(readers))), ("32_sets", readers * ROT),
+                           ("64_sets", (readers + extra) * (ROT // 2))):
             gc = torch.cuda.CUDAGraph()
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
@@ -426,13 +431,13 @@ def main():
                 stream.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(stream):
                     with torch.cuda.graph(gk, stream=stream):
-                        for r in readers:
+                        for r in readers * ROT:
                             rc = cal.hcrc_read_floor(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(),
                                                      r.w_norm.data_ptr(), r.scratch.data_ptr(), xs[T].data_ptr(),
                                                      stream.cuda_stream)
                             assert rc == hcr.HCR_OK, rc
                 torch.cuda.current_stream().wait_stream(stream)
-                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(readers)), 3)
                 del gk
             log(f"bench: calibration {key}: {calibration[key]}")
         # the pages' down shape (10 rows x a 1,280-column slab) and its last-arriver finish, as load / store /
@@ -447,13 +452,13 @@ def main():
                 stream.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(stream):
                     with torch.cuda.graph(gk, stream=stream):
-                        for r in readers:
+                        for r in readers * ROT:
                             rc = cal.hcrc_slab_pair(kind, T, r.w_down.data_ptr(), r.w_up.data_ptr(),
                                                     r.w_norm.data_ptr(), slab_sc.data_ptr(), xs[T].data_ptr(),
                                                     stream.cuda_stream)
                             assert rc == hcr.HCR_OK, rc
                 torch.cuda.current_stream().wait_stream(stream)
-                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(readers)), 3)
                 del gk
             log(f"bench: calibration {key}: {calibration[key]}")
         # the whole read in the pages' shape, with its arithmetic (hcrc_slab_read: slab down kernel, last-arriver
@@ -466,13 +471,13 @@ def main():
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
                 with torch.cuda.graph(gk, stream=stream):
-                    for r in readers:
+                    for r in readers * ROT:
                         rc = cal.hcrc_slab_read(T, r.w_down.data_ptr(), r.w_up.data_ptr(), r.w_norm.data_ptr(),
                                                 slab_sc.data_ptr(), xs[T].data_ptr(), None, None, outs[T].data_ptr(),
                                                 means[T].data_ptr(), stream.cuda_stream)
                         assert rc == hcr.HCR_OK, rc
             torch.cuda.current_stream().wait_stream(stream)
-            calibration["slab_read_us"][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+            calibration["slab_read_us"][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(readers)), 3)
             del gk
         log(f"bench: calibration slab_read_us: {calibration['slab_read_us']}")
         del slab_sc
@@ -489,12 +494,12 @@ def main():
                 stream.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(stream):
                     with torch.cuda.graph(gk, stream=stream):
-                        for r in readers:
+                        for r in readers * ROT:
                             rc = cal.hcrc_up_kernel(kind, T, r.w_up.data_ptr(), r.scratch.data_ptr(),
                                                     outs[T].data_ptr(), means[T].data_ptr(), stream.cuda_stream)
                             assert rc == hcr.HCR_OK, rc
                 torch.cuda.current_stream().wait_stream(stream)
-                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers)), 3)
+                calibration[key][T] = round(timed(gk, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(readers)), 3)
                 del gk
             log(f"bench: calibration {key}: {calibration[key]}")
         calibration["note"] = ("per T, graphs of 32 pairs on the read's grids and work-group sizes over the 32 rotated "
@@ -520,10 +525,11 @@ def main():
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             with torch.cuda.graph(ge, stream=stream):
-                for k, r in enumerate(readers):
-                    r.read(ex[k], ep[k], ei[k], out=outs[T], mean=means[T])
+                for _ in range(ROT):
+                    for k, r in enumerate(readers):
+                        r.read(ex[k], ep[k], ei[k], out=outs[T], mean=means[T])
         torch.cuda.current_stream().wait_stream(stream)
-        us = timed(ge, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(readers))
+        us = timed(ge, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * ROT * len(readers))
         full_epilogue[T] = {"us_per_read": round(us, 3),
                             "algorithmic_GBps": round(algorithmic_bytes(T, pending=True, inj=True) / us / 1e3, 1)}
         hashes.setdefault("full_epilogue", {})[T] = {"out": sha256_of(outs[T]), "mean": sha256_of(means[T])}
@@ -577,13 +583,13 @@ def main():
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             with torch.cuda.graph(gq, stream=stream):
-                for r, q in zip(readers, qsets):
+                for r, q in list(zip(readers, qsets)) * (ROT // 2):
                     for w, c, sc in ((r.w_down, q[0], q[1]), (r.w_up, q[2], q[3])):
                         rc = hcr.hcr_quantize_q8_0(w.data_ptr(), w.shape[0], w.shape[1], c.data_ptr(),
                                                    sc.data_ptr(), stream.cuda_stream)
                         assert rc == hcr.HCR_OK
         torch.cuda.current_stream().wait_stream(stream)
-        q_us = timed(gq, 5, 1) * 1000.0 / (5 * 2 * len(readers))
+        q_us = timed(gq, 5, 1) * 1000.0 / (5 * 2 * (ROT // 2) * len(readers))
         del gq
         q_bytes = R * S * D * (2 + 1) + R * S * D // 32 * 2  # BF16 read, codes and scales written
         q8_T_us, q8_T_gbps = {}, {}
@@ -592,10 +598,10 @@ def main():
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
                 with torch.cuda.graph(gq, stream=stream):
-                    for qr in q8_readers:
+                    for qr in q8_readers * (ROT // 2):
                         qr.read(xs[T], out=outs[T], mean=means[T])
             torch.cuda.current_stream().wait_stream(stream)
-            us = timed(gq, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * len(q8_readers))
+            us = timed(gq, args.per_t_reps, 2) * 1000.0 / (args.per_t_reps * (ROT // 2) * len(q8_readers))
             q8_T_us[T] = round(us, 3)
             q8_T_gbps[T] = round(algorithmic_bytes_q8(T) / us / 1e3, 1)
             if T <= TMAX:
@@ -629,13 +635,13 @@ def main():
             stream.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(stream):
                 with torch.cuda.graph(gm, stream=stream):
-                    for k in range(n_mv):
+                    for k in list(range(n_mv)) * (4 * ROT):
                         rc = hcr.hcr_matvec_bf16(mw[k].data_ptr(), rows, cols, T, mx.data_ptr(), my.data_ptr(),
                                                  stream.cuda_stream)
                         assert rc == hcr.HCR_OK
             torch.cuda.current_stream().wait_stream(stream)
-            reps = max(args.per_t_reps, 1) * 2
-            us = timed(gm, reps, 2) * 1000.0 / (reps * n_mv)
+            reps = max(args.per_t_reps, 1)
+            us = timed(gm, reps, 2) * 1000.0 / (reps * 4 * ROT * n_mv)
             b = rows * cols * 2 + T * cols * 4 + T * rows * 4
             mv_T_us[T] = round(us, 3)
             mv_T_gbps[T] = round(b / us / 1e3, 1)
@@ -647,7 +653,7 @@ def main():
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "frac": round(sum(mv_T_gbps.values()) / len(mv_T_gbps) / HBM_PEAK_GBPS, 4),
                                "best_frac": round(best / HBM_PEAK_GBPS, 4), "traffic": measured_matvec_traffic()},
-                  "note": "y = W x, BF16 weights, 1..4 columns; graphs of 8 calls over the rotated copies; "
+                  "note": "y = W x, BF16 weights, 1..4 columns; graphs of 256 calls, 32 passes over the 8 rotated copies; "
                           "not part of the timed step"}
         del mw
 
@@ -685,6 +691,27 @@ def main():
                   "note": "one HIP graph of the 96-read residual chain, distinct BF16 weight sets (1.26 GB)"}
         log(f"bench: window {window['us_per_window']} us ({window['us_per_read']} us/read, "
             f"{window['algorithmic_GBps']} GB/s)")
+        # the same window twice in one graph (the chain carried on through the same 96 sets): a replay of it
+        # takes 2 W + b, one of the one-window graph W + b, so W and the replay boundary b follow
+        g2 = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g2, stream=stream):
+                xx = wx0
+                for i in range(2 * n_win):
+                    wreaders[i % n_win].read(xx, wpend[i % n_win], None, out=wouts[i % n_win], mean=wmeans[i % n_win])
+                    xx = wouts[i % n_win]
+        torch.cuda.current_stream().wait_stream(stream)
+        w2ms = timed(g2, reps // 2, 2) / (reps // 2)
+        wms1 = timed(gw, reps, 2) / reps  # the one-window graph again, beside it
+        del g2
+        window["us_per_window_without_replay_boundary"] = round((w2ms - wms1) * 1000, 2)
+        window["graph_replay_boundary_us"] = round((2 * wms1 - w2ms) * 1000, 2)
+        window["replay_boundary_note"] = ("a graph of the window twice (192 chained reads) against the one-window "
+                                          "graph, timed beside it: W = t2 - t1, boundary = 2 t1 - t2 (the runtime's "
+                                          "cost of one graph replay, counted once in us_per_window)")
+        log(f"bench: window without the replay boundary {window['us_per_window_without_replay_boundary']} us "
+            f"(boundary {window['graph_replay_boundary_us']} us)")
         # the same chain with its weights resident in the MALL (16 sets, 210 MB, reused in turn): the bound
         # that prefetching the next read's weights into the MALL could reach
         del gw

@@ -226,6 +226,12 @@ __global__ __launch_bounds__(down_threads(T)) void hc_down(const void* __restric
 #pragma unroll
         for (int e = 0; e < CB; ++e) ss = __builtin_fmaf(xv[i].b[e], xv[i].b[e], ss);
         v[quad_pos(t, N)] = ss;
+        // pinned here: the compiler had sunk some tokens' sums of squares below the first wait for the
+        // weights (T = 3, 6, 7: 20-30 VALU instructions).  Measured on MI355X (bench.py --ab, one process,
+        // alternating builds, 6 rounds): the 96-read window 707.6 against 710.0 us; the sweep level
+        vm_pin(v[quad_pos(t, N)]);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) vm_pin(act[i][e]);
       }
     }
     if constexpr (EARLY) {
