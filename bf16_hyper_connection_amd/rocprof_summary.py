@@ -54,15 +54,21 @@ def kernel_key(name):
     # the calibration library (include/hcr_calib.h)
     if "cal_empty" in name:
         return ("cal_empty",)
-    m = re.search(r"cal_down_loads<(\d+)>", name)
+    m = re.search(r"cal_down_loads<(\d+), (true|false)>", name)  # (T, one store per work-group)
     if m:
-        return ("cal_down_loads", int(m.group(1)))
+        return ("cal_down_loads", int(m.group(1))) if m.group(2) == "false" else ("cal_down_loads_store", int(m.group(1)))
     m = re.search(r"cal_up_mfma_loads<(\d+)>", name)
     if m:
         return ("cal_up_loads", int(m.group(1)))
     m = re.search(r"cal_up_(valu|mfma)<(\d+)>", name)
     if m:
         return ("cal_up_" + m.group(1), int(m.group(2)))
+    m = re.search(r"cal_slab_read_down<(\d+), (true|false)>", name)
+    if m:
+        return ("cal_slab_read_down", int(m.group(1)), m.group(2) == "true")
+    m = re.search(r"cal_slab_read_up<(\d+), (true|false)>", name)
+    if m:
+        return ("cal_slab_read_up", int(m.group(1)), m.group(2) == "true")
     m = re.search(r"cal_slab_down<(\d+), (\d+)>", name)
     if m:
         return ("cal_slab_down", int(m.group(1)), int(m.group(2)))
@@ -329,6 +335,14 @@ def main():
                                                         "up_lo_loads_us": round(dur[("cal_slab_up", T)][0], 3)}
             slab_lines.append(f"| {T} | {dur[ks[0]][0]:.3f} | {dur[ks[1]][0]:.3f} | {dur[ks[2]][0]:.3f} | "
                               f"{dur[ks[2]][0] - dur[ks[1]][0]:+.3f} | {dur[('cal_slab_up', T)][0]:.3f} |")
+    sread_lines = []
+    for T in range(1, 9):
+        kd, ku = ("cal_slab_read_down", T, False), ("cal_slab_read_up", T, False)
+        rd, ru = ("down", T, 0, False, False), ("up", T, 0, False, False)
+        if kd in dur and ku in dur and rd in dur and ru in dur:
+            rec.setdefault("slab_read", {})[str(T)] = {"down_us": round(dur[kd][0], 3), "up_us": round(dur[ku][0], 3)}
+            sread_lines.append(f"| {T} | {dur[kd][0]:.3f} | {dur[ku][0]:.3f} | {dur[kd][0] + dur[ku][0]:.3f} | "
+                               f"{dur[rd][0]:.3f} | {dur[ru][0]:.3f} | {dur[rd][0] + dur[ru][0]:.3f} |")
     if ("cal_empty",) in dur:
         rec["cal_empty_avg_us"] = round(dur[("cal_empty",)][0], 3)
     if cal_lines:
@@ -350,6 +364,13 @@ def main():
                    "work-group of a row group sums the 8 slabs):", "",
                "| T | loads | + stores | + finish | the finish's cost | up kernel loading lo |", "|---|---|---|---|---|---|"]
         md += slab_lines
+    if sread_lines:
+        md += ["", "The whole read in the pages' shape with its arithmetic (`hcrc_slab_read`: the slab down kernel "
+                   "with its partials, sums of squares and last-arriver finish applying rs and writing lo, then the "
+                   "read's up kernel on lo alone; no pending write or injection) against the read, average µs per "
+                   "dispatch:", "",
+               "| T | slab down + finish | up on lo | sum | hc_down | hc_up_mfma | sum |",
+               "|---|---|---|---|---|---|---|"] + sread_lines
     if q in dur:
         md += ["", f"q8_quantize (one 320 x 10240 or 10240 x 320 matrix): {dur[q][0]:.3f} µs average over "
                    f"{dur[q][1]} calls."]
