@@ -59,8 +59,10 @@
 // weight loads are in flight.
 //
 // Loads: vector-memory loads complete in issue order, so every kernel issues
-// its small inputs first (x, w_norm; partials, injection, pending) and its
-// weight tile after them, all before any arithmetic; the weights go in the
+// the small inputs its arithmetic needs first (x, w_norm; partials,
+// injection) and its weight tile after them, all before any arithmetic (the
+// pending values, which only the epilogue needs, go behind the weights where
+// the up kernel waits for its loads itself); the weights go in the
 // order the arithmetic uses them (row by row in hc_down, K step by K step in
 // hc_up_mfma), and arithmetic that needs only the small inputs is kept ahead
 // of every use of the weights, so that it runs while they are in flight.

@@ -284,8 +284,9 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;  // an XCD's tiles are contiguous
   const int li = lane & 15, lg = lane >> 4;
-  // 1. small loads first: stream partials and injection for lo, pending for the epilogue, and (Q8_0)
-  //    the work-group's block scales: per stream s, rows s*2560 + c0 .. + 9 hold 200 contiguous bytes
+  // 1. small loads first: stream partials and injection for lo, pending for the epilogue (on the LDS path
+  //    after the weights instead, step 2), and (Q8_0) the work-group's block scales: per stream s, rows
+  //    s*2560 + c0 .. + 9 hold 200 contiguous bytes
   //    BF16 up to T = 12 (ALDS, up_weights_lds): every load of the kernel is untracked (ld*_untracked: the
   //    weights go straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.  A 4th wave
   //    (upm_threads: from T = 10, and below where it takes a round off the staging) has no tile: with ALDS it
@@ -331,19 +332,17 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   // A staging-only 4th wave on the LDS path has no epilogue lanes and loads no pending values (its loads are
   // untracked, so the branch adds no wait).  Measured on MI355X (bench.py --ab --ab-window, one process,
   // alternating builds, 6 rounds): the 96-read window (T = 6, pending on) from 721.3 to 712.6 us; skipping the
-  // tile waves' lanes outside the epilogue as well gave 715.3 us
+  // tile waves' lanes outside the epilogue as well gave 715.3 us.  On the LDS path the pending values are
+  // loaded after the weights (step 2): only the epilogue uses them, and loads complete in issue order, so they
+  // arrive right behind the last weights instead of holding the weights back (the window 706.7 against
+  // 710.8 us, the same A/B)
   float pend[S];
   const bool pload = !(ALDS && EXTRA) || __builtin_amdgcn_readfirstlane(wave) < 3;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const float* pp = pending + ((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1);
     pend[s] = 0.f;
-    if (PEND) {
-      if (!ALDS)
-        pend[s] = *pp;
-      else if (pload)
-        pend[s] = ld1_untracked(pp);
-    }
+    if (PEND && !ALDS) pend[s] = *pp;
   }
   __builtin_amdgcn_sched_barrier(0);  // keeps every small load ahead of the weight loads
   // 2. weights (A operand), tile = wave: row rw = 16 * wave + li of the work-group's 40 (rw & 3 = stream,
@@ -371,6 +370,11 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     if (!EXTRA || wave < 3)
       load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
                            lane, c0);
+    if (PEND && pload) {  // the pending values, behind the weights
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        pend[s] = ld1_untracked(pending + ((size_t)min(li, T - 1) * S + s) * D + c0 + min(cc, UP_COLS - 1));
+    }
   } else {
     const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
     const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
@@ -384,7 +388,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (ALDS) {  // the partials (and injection): all but the pending loads and the 10 weight loads
+  if constexpr (ALDS) {  // the partials (and injection): all but the 10 weight loads and the pending loads
     if (!EXTRA || wave < 3)
       vm_wait<(PEND ? S : 0) + 10>();
     else
@@ -460,6 +464,16 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   //    (one block) into a fresh accumulator, added times the block scales of the lane's 4 rows.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // every step's B operand read from LDS ahead of the first wait for the weights, so that a step waits only
+  // for its A read once its weights are in.  Measured on MI355X (bench.py --ab, one process, alternating
+  // builds, 4 rounds): 0.04-0.08 us less per read at T = 1..8, 0.19 us at T = 9..12, 0.03-0.05 us at
+  // T = 13..16, 0.06-0.12 us for the Q8_0 copies from T = 4; the results the same bit for bit
+  uint4 bpre[R / 32], lpre[PACK ? 1 : R / 32];
+#pragma unroll
+  for (int m = 0; m < R / 32; ++m) {
+    bpre[m] = bh[m][lg][li ^ ((4 * m + lg) & 15)];  // column li of B, swizzled as staged
+    if constexpr (!PACK) lpre[m] = bl[m][lg][li ^ ((4 * m + lg) & 15)];
+  }
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
     bf16x8 am;
@@ -467,18 +481,18 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
       am = codes_bf16(qa[m]);
     } else if constexpr (ALDS) {
       // chunk 4 m + lg of tile row li: line p = m / 2, load 2 p + li / 8, lane 8 (li % 8) + (chunk % 8) ^ (li % 8);
-      // line p's two loads are done once no more than the 8 - 2 p weight loads after them are in flight
-      if (m % 2 == 0) vm_wait_n(8 - m);
+      // line p's two loads are done once no more than the 8 - 2 p weight loads after them (and the pending
+      // loads behind those) are in flight
+      if (m % 2 == 0) vm_wait_n(8 - m + (PEND ? S : 0));
       const int h = li >> 3, r8 = li & 7, ep = (4 * m + lg) & 7;
       am = *reinterpret_cast<const bf16x8*>(a_sm + wave * A_REGION + (2 * (m >> 1) + h) * A_LOAD_STRIDE +
                                             16 * (8 * r8 + (ep ^ r8)));
     } else {
       am = __builtin_bit_cast(bf16x8, a[m]);
     }
-    const int bc = li ^ ((4 * m + lg) & 15);  // column li of B, swizzled as staged
-    f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bh[m][lg][bc]), Q8 ? zero : acc, 0, 0, 0);
+    f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bpre[m]), Q8 ? zero : acc, 0, 0, 0);
     if constexpr (!PACK)
-      pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bl[m][lg][bc]), pm, 0, 0, 0);
+      pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, lpre[m]), pm, 0, 0, 0);
     if constexpr (Q8) {
       const f32x4 dm = *reinterpret_cast<const f32x4*>(sc_sm + (min(cc, UP_COLS - 1) * (R / Q8_BLOCK) + m) * S);
 #pragma unroll
@@ -491,7 +505,8 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
 #pragma unroll
     for (int s = 0; s < S; ++s) acc[s] += dpp<0x128>(acc[s]);  // row_ror:8
   }
-  if constexpr (ALDS && PEND) {  // the pending loads, older than the weight loads, are done since step 0's wait
+  if constexpr (ALDS && PEND) {  // the pending loads, the youngest of the kernel
+    vm_wait<0>();
 #pragma unroll
     for (int s = 0; s < S; ++s) vm_pin(pend[s]);
   }
