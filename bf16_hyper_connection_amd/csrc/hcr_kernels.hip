@@ -277,16 +277,36 @@ __global__ __launch_bounds__(down_threads(T)) void hc_down(const void* __restric
           for (int e = 0; e < CB; ++e) wv[CA + e] *= db;
         }
       }
+      if constexpr (FMT == FMT_BF16 || DECODE) {
+        // every token's chain over the CA columns of the row's first load, then (after a scheduling barrier)
+        // over the CB columns of its second: each chain keeps its order, and the wait for the second load
+        // comes after every product of the first.  The compiler had placed it after the first token's CA
+        // products, so that at T = 6 / 8, 53 / 73 FMAs of the last row waited for the last load instead of
+        // 12 / 16.  Measured on MI355X (bench.py --ab, one process, alternating builds, 5-6 rounds, the results
+        // bitwise the same): the 96-read window 701.8 against 705.6 us, 0.03 us less per read at T = 6..8,
+        // level at T = 1..5 and for the Q8_0 copies
+        float acc[TG];
 #pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        const int t = grp * TG + i;
-        if (t < T) {
-          if constexpr (FMT == FMT_BF16 || DECODE) {
-            float acc = 0.f;
+        for (int i = 0; i < TG; ++i) {
+          acc[i] = 0.f;
 #pragma unroll
-            for (int e = 0; e < NC; ++e) acc = __builtin_fmaf(wv[e], act[i][e], acc);
-            v[quad_pos((r + 1) * T + t, N)] = acc;
-          } else {
+          for (int e = 0; e < CA; ++e) acc[i] = __builtin_fmaf(wv[e], act[i][e], acc[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          const int t = grp * TG + i;
+          if (t < T) {
+#pragma unroll
+            for (int e = CA; e < NC; ++e) acc[i] = __builtin_fmaf(wv[e], act[i][e], acc[i]);
+            v[quad_pos((r + 1) * T + t, N)] = acc[i];
+          }
+        }
+      } else {  // Q8_0 below 4 tokens: one chain per block chunk, each times its block's scale
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          const int t = grp * TG + i;
+          if (t < T) {
             float a8 = 0.f;
 #pragma unroll
             for (int e = 0; e < CA; ++e) a8 = __builtin_fmaf(wv[e], act[i][e], a8);
