@@ -112,9 +112,8 @@ __global__ __launch_bounds__(down_threads(T)) void cal_down_loads(const uint16_t
   }
 }
 
-// hc_up_mfma<T>'s loads: partials, then one 16-row tile of W_up per wave.  Up to T = 12 (up_weights_lds) the
-// weights go straight into LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads
-// none); from T = 13 into registers in the operand layout (10 K steps).
+// hc_up_mfma<T>'s loads: partials, then one 16-row tile of W_up per wave.  The BF16 weights go straight into
+// LDS through load_a_lds, the read's own function (10 loads per wave; a 4th wave loads none).
 template <int T>
 __global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(const uint16_t* __restrict__ w_up,
                                                          const float* __restrict__ part) {

@@ -108,11 +108,12 @@ constexpr int upm_threads(int T, int fmt) {
 static_assert(upm_threads(3, FMT_BF16) == 256 && upm_threads(4, FMT_BF16) == 192 && upm_threads(7, FMT_BF16) == 192 &&
                   upm_threads(8, FMT_BF16) == 256 && upm_threads(9, FMT_Q8_0) == 192,
               "the 4th wave where it saves a staging round");
-// BF16 up weights straight into LDS (global_load_lds_dwordx4, whole 128-byte lines) up to T = 12, in the
-// matrix-core operand layout into registers from T = 13.  Measured on MI355X (bench.py --ab, one process,
-// alternating builds, 4 rounds, the results bitwise the same): the LDS path 0.08-0.10 us faster per read at
-// T = 10..12 and 0.08-0.12 us slower at T = 13..16
-constexpr bool up_weights_lds(int T, int fmt) { return fmt == FMT_BF16 && T <= 12; }
+// BF16 up weights straight into LDS (global_load_lds_dwordx4, whole 128-byte lines) at every T; Q8_0 codes go
+// into registers in the matrix-core operand layout.  Measured on MI355X (bench.py --ab, one process, alternating
+// builds, 4 rounds, the results bitwise the same), against the operand layout in registers: the LDS path
+// 0.08-0.10 us faster per read at T = 10..12, and, once every step's B operand is read ahead of the first weight
+// wait, 0.07-0.14 us faster at T = 13..16 as well (slower by 0.08-0.12 there before)
+constexpr bool up_weights_lds(int T, int fmt) { return fmt == FMT_BF16 && T >= 1; }
 constexpr int Q8_BLOCK = 32;
 static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % down_ca(1) == 0 &&
                   Q8_BLOCK % down_ca(TMAX) == 0 && Q8_BLOCK % 8 == 0,

@@ -287,7 +287,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   // 1. small loads first: stream partials and injection for lo, pending for the epilogue (on the LDS path
   //    after the weights instead, step 2), and (Q8_0) the work-group's block scales: per stream s, rows
   //    s*2560 + c0 .. + 9 hold 200 contiguous bytes
-  //    BF16 up to T = 12 (ALDS, up_weights_lds): every load of the kernel is untracked (ld*_untracked: the
+  //    BF16 (ALDS, up_weights_lds): every load of the kernel is untracked (ld*_untracked: the
   //    weights go straight into LDS, step 2) and waited for explicitly; otherwise ordinary loads.  A 4th wave
   //    (upm_threads: from T = 10, and below where it takes a round off the staging) has no tile: with ALDS it
   //    loads no weights.
@@ -467,7 +467,8 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   // every step's B operand read from LDS ahead of the first wait for the weights, so that a step waits only
   // for its A read once its weights are in.  Measured on MI355X (bench.py --ab, one process, alternating
   // builds, 4 rounds): 0.04-0.08 us less per read at T = 1..8, 0.19 us at T = 9..12, 0.03-0.05 us at
-  // T = 13..16, 0.06-0.12 us for the Q8_0 copies from T = 4; the results the same bit for bit
+  // T = 13..16 (weights then in registers), 0.06-0.12 us for the Q8_0 copies from T = 4; the results the same
+  // bit for bit
   uint4 bpre[R / 32], lpre[PACK ? 1 : R / 32];
 #pragma unroll
   for (int m = 0; m < R / 32; ++m) {
