@@ -31,6 +31,10 @@ HIPCC_FLAGS = [
     # MI355X (cold read, one process, alternating with a build without it, 3 rounds): 0.08 us less per read
     # on the mean over T = 1..8
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
+    # matrix-core results in VGPRs rather than accumulation registers, so that the Q8_0 up kernel's per-block
+    # scaling reads them without a v_accvgpr_read each.  Measured on MI355X (bench.py --ab, one process,
+    # alternating builds, 3-4 rounds): the Q8_0 read 0.04-0.09 us faster per read from T = 4, BF16 level
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 
@@ -61,8 +65,8 @@ def _code_only(text):
 
 def source_hash():
     """sha256 over the code of libhcr.so's sources (its csrc/ files and headers, and include/hcr.h; not the
-    calibration library's), comments and whitespace left out; measurements taken with hardware counters
-    are valid only for the code they were taken on."""
+    calibration library's), comments and whitespace left out, and the compiler flags; measurements taken
+    with hardware counters are valid only for the code they were taken on."""
     h = hashlib.sha256()
     files = sorted(f for f in os.listdir(CSRC)
                    if f.endswith((".hip", ".h", ".cpp")) and f not in CALIB_SOURCES)
@@ -70,6 +74,7 @@ def source_hash():
     for path in paths:
         with open(path) as fh:
             h.update(os.path.basename(path).encode() + b"\0" + _code_only(fh.read()).encode() + b"\0")
+    h.update(" ".join(HIPCC_FLAGS).encode())  # the code the compiler makes of them
     return h.hexdigest()
 
 

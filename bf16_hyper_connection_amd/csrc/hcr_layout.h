@@ -95,18 +95,19 @@ static_assert(R == 32 * 8 + 32 * 2 && D % UP_COLS == 0 && UP_WAVE_ROWS % 2 == 0,
 enum : int { FMT_BF16 = 0, FMT_Q8_0 = 1 };
 
 // matrix-core up kernel: one 16-row tile of the 40 rows per wave (3 waves), plus a 4th wave with no tile when it
-// takes a round off the lo staging (T * R / 4 items, one per thread and round).  BF16 from T = 10, and below
-// where it saves a round (T = 3, 5, 6, 8, 9; its weights go straight into LDS, so the 4th wave loads none):
+// takes a round off the lo staging (T * R / 4 items, one per thread and round): from T = 10, and below where it
+// saves a round (T = 3, 5, 6, 8, 9).  BF16 (its weights go straight into LDS, so the 4th wave loads none):
 // measured 0.17 us faster per read at T = 8 and 0.02-0.03 at T = 3, 5, 6; at T = 4 and 7, where the rounds stay
 // the same, 0.15 and 0.22 us slower.  More staging waves, although they take further rounds off, were slower:
-// 5 waves at T = 7 / 8 by 0.65 / 0.39 us, 8 waves at T = 6 by 0.63 us.  Q8_0 copies from T = 10 (its 4th wave
-// re-loads the third tile's codes).
+// 5 waves at T = 7 / 8 by 0.65 / 0.39 us, 8 waves at T = 6 by 0.63 us.  Q8_0 copies (the 4th wave re-loads the
+// third tile's codes): 0.08-0.13 us faster per read at T = 5, 6, 8 and 0.2 us at T = 9 (bench.py --ab --ab-q8,
+// one process, alternating builds, 3 rounds)
 constexpr int staging_rounds(int T, int threads) { return (T * (R / 4) + threads - 1) / threads; }
-constexpr int upm_threads(int T, int fmt) {
-  return T >= 10 || (fmt == FMT_BF16 && staging_rounds(T, 256) < staging_rounds(T, 192)) ? 256 : 192;
+constexpr int upm_threads(int T, int /* fmt: the same rule for both formats */) {
+  return T >= 10 || staging_rounds(T, 256) < staging_rounds(T, 192) ? 256 : 192;
 }
 static_assert(upm_threads(3, FMT_BF16) == 256 && upm_threads(4, FMT_BF16) == 192 && upm_threads(7, FMT_BF16) == 192 &&
-                  upm_threads(8, FMT_BF16) == 256 && upm_threads(9, FMT_Q8_0) == 192,
+                  upm_threads(8, FMT_BF16) == 256 && upm_threads(9, FMT_Q8_0) == 256 && upm_threads(4, FMT_Q8_0) == 192,
               "the 4th wave where it saves a staging round");
 // BF16 up weights straight into LDS (global_load_lds_dwordx4, whole 128-byte lines) at every T; Q8_0 codes go
 // into registers in the matrix-core operand layout.  Measured on MI355X (bench.py --ab, one process, alternating
