@@ -56,7 +56,10 @@ constexpr int UP_ROWS = UP_COLS * S;                         // 40
 constexpr int UP_WAVE_ROWS = UP_ROWS / (UP_THREADS / 64);    // 10
 constexpr int UP_ITERS = UP_WAVE_ROWS / 2;                   // 5 (two rows per iteration, one per half-wave)
 constexpr int UP_MFMA_FROM = 1;  // BF16 up projection on the matrix cores at every T (measured faster at T = 1 too)
-constexpr int UP_MFMA_FROM_Q8 = 4;  // the same for Q8_0 copies (their codes are widened per K step)
+// the same for Q8_0 copies from T = 3 (their codes are widened per K step).  Measured on MI355X (bench.py --ab
+// --ab-q8, one process, alternating builds, 4 rounds): 0.23 us faster per read at T = 3 than the vector-ALU
+// kernel, 0.15 us slower at T = 2
+constexpr int UP_MFMA_FROM_Q8 = 3;
 
 // ---- scratch (bytes) ----
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
