@@ -23,7 +23,7 @@
  * parts); summation orders are fixed, so a call is bitwise reproducible, also
  * as a replayed HIP graph.  A token's results are the same bit for bit
  * whatever the other tokens of the window within one range of T: BF16 weights
- * T = 1..8 and T = 9..16, Q8_0 copies T = 1..3, 4..8 and 9..16.
+ * T = 1..8 and T = 9..16, Q8_0 copies T = 1..2, 3..8 and 9..16.
  *
  * Memory. Every pointer is a device pointer the caller owns (the library
  * allocates nothing on the device and never frees caller memory).  Layouts
