@@ -252,7 +252,7 @@ def verify_window(n_reads=96, T=6, base=4):
 
 
 def numerics_stress(seed=5, T=8, n_sets=32):
-    """T = 8, heavy-tailed x over six decades of stream RMS, near-tie rows, pending and inj on."""
+    """T tokens (8 by default), heavy-tailed x over six decades of stream RMS, near-tie rows, pending and inj on."""
     ws = []
     for k in range(n_sets):
         w = weight_set(seed, k)

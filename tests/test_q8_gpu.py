@@ -112,13 +112,16 @@ def test_q8_wide_windows_epilogue_variants(q8set, T, with_pending, with_inj):
     check_read(q8set.reader, T, out, mean, q8set.ref_read(x, p, inj), f"Q8_0 T={T} p={with_pending} i={with_inj}")
 
 
-def test_q8_numerics_stress():
-    """Heavy-tailed x (stream RMS 1e-3..1e3), near-duplicate W_down rows, pending and inj, 4 sets, T = 8."""
-    c = gen.numerics_stress(15, T=8, n_sets=4)
+@pytest.mark.parametrize("T", [2, 3, 8])
+def test_q8_numerics_stress(T):
+    """Heavy-tailed x (stream RMS 1e-3..1e3), near-duplicate W_down rows, pending and inj, 4 sets; T = 2 and 3
+    sit on either side of the switch from the vector-ALU to the matrix-core up kernel."""
+    c = gen.numerics_stress(15, T=T, n_sets=4)
     for k, w in enumerate(c["weights"]):
         s = Q8Set(w)
         out, mean = s.reader.read(to_dev(c["x"][k]), to_dev(c["pending"][k]), to_dev(c["inj"][k]))
-        check_read(s.reader, 8, out, mean, s.ref_read(c["x"][k], c["pending"][k], c["inj"][k]), f"Q8_0 stress {k}")
+        check_read(s.reader, T, out, mean, s.ref_read(c["x"][k], c["pending"][k], c["inj"][k]),
+                   f"Q8_0 stress T={T} set {k}")
 
 
 @pytest.mark.parametrize("lo_t,hi_t,windows", [
@@ -140,7 +143,7 @@ def test_q8_token_results_do_not_depend_on_T(q8set, lo_t, hi_t, windows):
         assert torch.equal(o, of[a:b]) and torch.equal(m, mf[a:b]), f"tokens {a}..{b - 1}"
 
 
-@pytest.mark.parametrize("T", [1, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 16])
 def test_q8_graph_replay_bitwise(q8set, T):
     r = q8set.reader
     xd, pd, idd = to_dev(gen.activations(17, T)), to_dev(gen.pending(17, T)), to_dev(gen.injection(17, T))
