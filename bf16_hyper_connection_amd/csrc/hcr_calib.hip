@@ -120,8 +120,7 @@ __global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(co
   constexpr int NT = upm_threads(T, FMT_BF16);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c0 = up_tile(blockIdx.x) * UP_COLS;
-  const int li = lane & 15, lg = lane >> 4;
-  constexpr bool ALDS = up_weights_lds(T, FMT_BF16);
+  static_assert(up_weights_lds(T, FMT_BF16), "the read's BF16 up weights go straight into LDS");
   // the partials first (issued before the weights, consumed after them, as in the read)
   constexpr int ITEMS = T * (R / 4);
   constexpr int NI = (ITEMS + NT - 1) / NT;
@@ -132,34 +131,22 @@ __global__ __launch_bounds__(upm_threads(T, FMT_BF16)) void cal_up_mfma_loads(co
     const int t = it / (R / 4), k = 4 * (it % (R / 4));
 #pragma unroll
     for (int ss = 0; ss < S; ++ss)
-      pv[n][ss] = ALDS ? ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k) : ld4(part + ((size_t)ss * TMAX + t) * R + k);
+      pv[n][ss] = ld4_untracked(part + ((size_t)ss * TMAX + t) * R + k);
   }
   __builtin_amdgcn_sched_barrier(0);
   constexpr int A_REGION = 10 * A_LOAD_STRIDE;
-  __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];
-  uint4 a[ALDS ? 1 : R / 32];
-  if constexpr (ALDS) {
-    if (NT == 192 || wave < 3) load_a_lds<A_REGION>(w_up, lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave), lane, c0);
-    vm_wait<0>();
+  __shared__ __attribute__((aligned(16))) unsigned char a_sm[3 * A_REGION];
+  if (NT == 192 || wave < 3) load_a_lds<A_REGION>(w_up, lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave), lane, c0);
+  vm_wait<0>();
 #pragma unroll
-    for (int n = 0; n < NI; ++n)
+  for (int n = 0; n < NI; ++n)
 #pragma unroll
-      for (int ss = 0; ss < S; ++ss) vm_pin(pv[n][ss]);
-  } else {
-    const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
-    const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
-#pragma unroll
-    for (int m = 0; m < R / 32; ++m) a[m] = *reinterpret_cast<const uint4*>(w_up + j * R + 32 * m + 8 * lg);
-  }
+    for (int ss = 0; ss < S; ++ss) vm_pin(pv[n][ss]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int n = 0; n < NI; ++n)
 #pragma unroll
     for (int ss = 0; ss < S; ++ss) use(pv[n][ss]);
-  if constexpr (!ALDS) {
-#pragma unroll
-    for (int m = 0; m < R / 32; ++m) use(a[m]);
-  }
 }
 
 // ---- the pages' down-kernel shape and finish, as loads (and stores, and the finish) only

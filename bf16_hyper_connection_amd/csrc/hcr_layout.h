@@ -117,7 +117,7 @@ static_assert(upm_threads(3, FMT_BF16) == 256 && upm_threads(4, FMT_BF16) == 192
 // builds, 4 rounds, the results bitwise the same), against the operand layout in registers: the LDS path
 // 0.08-0.10 us faster per read at T = 10..12, and, once every step's B operand is read ahead of the first weight
 // wait, 0.07-0.14 us faster at T = 13..16 as well (slower by 0.08-0.12 there before)
-constexpr bool up_weights_lds(int T, int fmt) { return fmt == FMT_BF16 && T >= 1; }
+constexpr bool up_weights_lds(int /* T: the same at every T */, int fmt) { return fmt == FMT_BF16; }
 constexpr int Q8_BLOCK = 32;
 static_assert(D % Q8_BLOCK == 0 && R % Q8_BLOCK == 0 && 256 % Q8_BLOCK == 0 && Q8_BLOCK % down_ca(1) == 0 &&
                   Q8_BLOCK % down_ca(TMAX) == 0 && Q8_BLOCK % 8 == 0,

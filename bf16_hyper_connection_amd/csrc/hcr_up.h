@@ -355,17 +355,17 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
   //    at byte i * 1152 of the region (A_LOAD_STRIDE), so the 8 rows of load 2 p sit at 0 and those of load
   //    2 p + 1 at 128 modulo 256: the read-back of one chunk's 16 rows meets 16 distinct LDS bank groups.  The
   //    third tile's rows 40..47 load rows 32..39 again (their products are not stored).
-  //    Otherwise in the operand layout, into registers: lane (li, lg) loads row rw, K 32 m + 8 lg.  No load
-  //    is conditional: rows 40..47 of the third tile re-load row 39, and a 4th wave re-loads the
-  //    third tile's rows, cache hits whose results are never stored (a branch around loads, even a
-  //    wave-uniform one, makes the compiler wait for them before the first barrier).  Non-temporal, except
+  //    Q8_0 codes in the operand layout, into registers: lane (li, lg) loads the 8 codes of row rw at
+  //    K 32 m + 8 lg.  No load is conditional: rows 40..47 of the third tile re-load row 39, and a 4th wave
+  //    re-loads the third tile's rows, cache hits whose results are never stored (a branch around loads, even
+  //    a wave-uniform one, makes the compiler wait for them before the first barrier).  Non-temporal, except
   //    with a 4th wave: its repeats of the third tile's rows are separate load instructions, which then
-  //    missed in L2 (measured 0.1-0.17 us slower per read at T = 10..16, before T = 10..12 took the LDS path).
+  //    missed in L2 (measured with BF16 weights on this path: 0.1-0.17 us slower per read at T = 10..16).
   constexpr int A_REGION = 10 * A_LOAD_STRIDE;
   static_assert(R == 320, "5 lines of 128 bytes per BF16 row, 10 loads per wave");
   __shared__ __attribute__((aligned(16))) unsigned char a_sm[ALDS ? 3 * A_REGION : 16];
-  uint4 a[ALDS || Q8 ? 1 : R / 32];  // BF16 in registers: 8 weights per step
-  uint2 qa[Q8 ? R / 32 : 1];         // Q8_0: 8 codes per step
+  static_assert(ALDS || Q8, "BF16 weights always go straight into LDS (up_weights_lds)");
+  uint2 qa[Q8 ? R / 32 : 1];  // Q8_0: 8 codes per step
   if constexpr (ALDS) {
     if (!EXTRA || wave < 3)
       load_a_lds<A_REGION>(static_cast<const uint16_t*>(w_up), lds_addr(a_sm), __builtin_amdgcn_readfirstlane(wave),
@@ -379,13 +379,9 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     const int rw = min(16 * min(wave, 2) + li, UP_ROWS - 1);
     const size_t j = (size_t)(rw & 3) * D + c0 + (rw >> 2);
 #pragma unroll
-    for (int m = 0; m < R / 32; ++m) {
-      if constexpr (Q8)
-        qa[m] = NTW ? ldw8(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg)
-                    : *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
-      else
-        a[m] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_up) + j * R + 32 * m + 8 * lg);
-    }
+    for (int m = 0; m < R / 32; ++m)
+      qa[m] = NTW ? ldw8(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg)
+                  : *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(w_up) + j * R + 32 * m + 8 * lg);
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (ALDS) {  // the partials (and injection): all but the 10 weight loads and the pending loads
@@ -480,7 +476,7 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
     bf16x8 am;
     if constexpr (Q8) {
       am = codes_bf16(qa[m]);
-    } else if constexpr (ALDS) {
+    } else {
       // chunk 4 m + lg of tile row li: line p = m / 2, load 2 p + li / 8, lane 8 (li % 8) + (chunk % 8) ^ (li % 8);
       // line p's two loads are done once no more than the 8 - 2 p weight loads after them (and the pending
       // loads behind those) are in flight
@@ -488,8 +484,6 @@ __device__ __forceinline__ void hc_up_mfma_body(const void* __restrict__ w_up, c
       const int h = li >> 3, r8 = li & 7, ep = (4 * m + lg) & 7;
       am = *reinterpret_cast<const bf16x8*>(a_sm + wave * A_REGION + (2 * (m >> 1) + h) * A_LOAD_STRIDE +
                                             16 * (8 * r8 + (ep ^ r8)));
-    } else {
-      am = __builtin_bit_cast(bf16x8, a[m]);
     }
     f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, __builtin_bit_cast(bf16x8, bpre[m]), Q8 ? zero : acc, 0, 0, 0);
     if constexpr (!PACK)
